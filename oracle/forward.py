@@ -1,0 +1,87 @@
+"""Oracle target forward over all B*(K+1) verification positions (fp64).
+
+What the pages fix: the target scores every drafted position in a single
+forward pass that reads its weights once (onlylabs/Cohere "Hardware Aware
+Dynamic Speculative Decoding", section "Hardware-aware dynamic SD": the
+target processes BS x (K+1) tokens; publishertech, section 1 "The
+Speculative Cycle").  The pages define no architecture; the synthetic target
+is the plain reading of "RMSNorm -> up -> SiLU -> down -> LM head": a stack of
+pre-norm residual MLP blocks without gate or bias, then a final RMSNorm and
+the LM head.  Rows never interact (there is no attention), so every row is
+computed independently.
+
+Numerics: fp64 throughout, except that the matmul inputs -- the normed
+activations a, the SiLU output s and the final normed activation a_f -- are
+rounded to bf16 (round to nearest even) when the weights are bf16, because
+the product is defined as bf16 inputs with fp32-or-better accumulation.  With
+fp32 weights nothing is rounded.
+
+Pinned by: torch.nn.functional (rms_norm, silu, linear) in float64 composed
+in the same block order; special cases (zero down weights leave h unchanged;
+zero layers reduce to the head on norm(hidden)); RMSNorm's scale invariance;
+bf16 rounding against torch's float32 -> bfloat16 conversion.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+RMS_EPS = 1e-5
+_HEAD_ROWS = 8192
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value (8 significant bits,
+    ties to even).  x = m * 2^e with 0.5 <= |m| < 1; keep round(m * 2^8)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # np.rint: ties to even
+
+
+def weights_f64(w: np.ndarray, lo: int | None = None, hi: int | None = None) -> np.ndarray:
+    """Rows [lo, hi) of a stored weight matrix as fp64 (bf16 patterns are
+    uint16; fp32 matrices pass through).  The upcast is exact."""
+    part = w[lo:hi]
+    if part.dtype == np.uint16:
+        return (part.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return part.astype(np.float64)
+
+
+def rmsnorm(h: np.ndarray, g: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """h / sqrt(mean(h^2) + eps) * g, per row."""
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps) * g
+
+
+def silu(u: np.ndarray) -> np.ndarray:
+    """u * sigmoid(u) = u / (1 + exp(-u))."""
+    return u / (1.0 + np.exp(-u))
+
+
+def head(a_f: np.ndarray, w_head: np.ndarray) -> np.ndarray:
+    """Logits a_f . W_head^T, taking the head in row blocks to bound memory."""
+    V = w_head.shape[0]
+    out = np.empty((a_f.shape[0], V), dtype=np.float64)
+    for lo in range(0, V, _HEAD_ROWS):
+        hi = min(lo + _HEAD_ROWS, V)
+        out[:, lo:hi] = a_f @ weights_f64(w_head, lo, hi).T
+    return out
+
+
+def final_activation(model: dict, hidden: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """Run the L blocks and the final norm; returns a_f [rows, d] (fp64)."""
+    rnd = bf16_round if model["w_up"].dtype == np.uint16 else (lambda v: v)
+    h = np.asarray(hidden, dtype=np.float64)
+    g = np.asarray(model["gain"], dtype=np.float64)
+    L = model["w_up"].shape[0]
+    for l in range(L):
+        a = rnd(rmsnorm(h, g[l], eps))
+        s = rnd(silu(a @ weights_f64(model["w_up"][l]).T))
+        h = h + s @ weights_f64(model["w_down"][l]).T
+    return rnd(rmsnorm(h, g[L], eps))
+
+
+def forward(model: dict, hidden: np.ndarray, heads=("w_head",), eps: float = RMS_EPS):
+    """Logits [rows, V] (fp64) for each requested head of ``model``.
+    Returns one array, or a tuple when several heads are asked for."""
+    a_f = final_activation(model, hidden, eps)
+    outs = tuple(head(a_f, model[name]) for name in heads)
+    return outs[0] if len(outs) == 1 else outs

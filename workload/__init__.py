@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the speculative-decoding verification step.
+
+This module only draws random numbers and lays them out; it holds none of the
+verification arithmetic (no norm, no matmul, no softmax, no sampling rule).
+Both the CPU oracle and the GPU path consume exactly the arrays made here.
+
+Workloads (shapes and distributions of the synthetic targets):
+
+* ``tiny-fp32``             d=256, ffn=1024, L=2, V=4096, fp32 weights with
+                            variance 1/d, B=1, K=4, sigma=0.5, T=1.
+* ``8b-shaped-b1-k4``       d=4096, ffn=14336, L=8, V=32000, bf16 weights with
+                            std 0.02, B=1, K=4, sigma=0.3, T=1.
+* ``8b-shaped-sweep``       the same stack, B in {1,4,16,64} x K in {1,2,4,8}.
+* ``70b-layer-share-b8-k4`` d=8192, ffn=28672, L=4, V=128256, bf16, B=8, K=4,
+                            sigma=0.3, T=1 and T=0.
+* ``large-batch-b256-k2``   d=4096, ffn=14336, L=8, V=128256, bf16, B=256,
+                            K=2, sigma=0.5, T=0.7.
+
+The draft model is an EAGLE-style head that reads the target's own final
+hidden state (klu.ai glossary, "Variants: Draft Models, EAGLE, Medusa, and
+Model-Free Methods"): its head weight is ``W_head + sigma * E`` with ``E``
+distributed like ``W_head``, so sigma alone sets how far q is from p.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "SWEEP_B", "SWEEP_K", "SWEEP_SIGMA",
+    "make_model", "make_hidden", "make_synthetic_logits", "make_random_tokens",
+    "bf16_bits_to_f32", "f32_to_bf16_bits",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    d: int
+    ffn: int
+    n_layers: int
+    vocab: int
+    wdtype: str          # "f32" or "bf16"
+    B: int
+    K: int
+    sigma: float
+    temperature: float
+    init: str            # "var_inv_d" (variance 1/d) or "std_0.02"
+    seed: int = 0
+
+    @property
+    def M(self) -> int:
+        return self.B * (self.K + 1)
+
+    @property
+    def weight_std(self) -> float:
+        return float(np.sqrt(1.0 / self.d)) if self.init == "var_inv_d" else 0.02
+
+    def with_batch(self, B: int, K: int, **kw) -> "Workload":
+        return replace(self, B=B, K=K, **kw)
+
+    def weight_elems(self) -> int:
+        return self.n_layers * 2 * self.d * self.ffn + self.vocab * self.d
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny-fp32", 256, 1024, 2, 4096, "f32", 1, 4, 0.5, 1.0, "var_inv_d"),
+        Workload("8b-shaped-b1-k4", 4096, 14336, 8, 32000, "bf16", 1, 4, 0.3, 1.0, "std_0.02"),
+        Workload("8b-shaped-sweep", 4096, 14336, 8, 32000, "bf16", 1, 1, 0.1, 1.0, "std_0.02"),
+        Workload("70b-layer-share-b8-k4", 8192, 28672, 4, 128256, "bf16", 8, 4, 0.3, 1.0, "std_0.02"),
+        Workload("large-batch-b256-k2", 4096, 14336, 8, 128256, "bf16", 256, 2, 0.5, 0.7, "std_0.02"),
+    ]
+}
+SWEEP_B = (1, 4, 16, 64)
+SWEEP_K = (1, 2, 4, 8)
+SWEEP_SIGMA = (0.1, 0.5)
+
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+# Stream ids keep every tensor's draws independent of every other tensor's.
+_STREAM = {"w_up": 1, "w_down": 2, "w_head": 3, "e_head": 4, "hidden": 5,
+           "logits_t": 6, "logits_noise": 7, "tokens": 8}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite fp32 values to bf16 (round to nearest, ties to even);
+    returns the 16-bit patterns as uint16."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> 16) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(shape, std: float, seed: int, stream: int, sub: int = 0) -> np.ndarray:
+    """fp32 N(0, std^2) array; drawn in fixed chunks, each from its own
+    PCG64 stream, so the result does not depend on the thread count."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    chunks = [(i, min(i + _CHUNK, n)) for i in range(0, n, _CHUNK)]
+
+    def fill(ci):
+        lo, hi = chunks[ci]
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, sub, ci])))
+        g.standard_normal(out=out[lo:hi], dtype=np.float32)
+        if std != 1.0:
+            out[lo:hi] *= np.float32(std)
+
+    if len(chunks) == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(len(chunks))))
+    return out.reshape(shape)
+
+
+def _as_weight(x: np.ndarray, wdtype: str) -> np.ndarray:
+    if wdtype == "f32":
+        return x
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
+    n = flat_in.size
+
+    def conv(lo):
+        hi = min(lo + _CHUNK, n)
+        flat_out[lo:hi] = f32_to_bf16_bits(flat_in[lo:hi])
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(conv, range(0, n, _CHUNK)))
+    return out
+
+
+def make_model(w: Workload, sigma: float | None = None, draft_head: bool = True) -> dict:
+    """Target weights (row-major [out, in]) plus the draft head.
+
+    Returns a dict with ``w_up`` [L, ffn, d], ``w_down`` [L, d, ffn],
+    ``gain`` [L+1, d] fp32 (ones; the last row is the final norm),
+    ``w_head`` [V, d] and, if asked, ``w_draft_head`` [V, d].  bf16 tensors
+    are uint16 bit patterns; fp32 tensors are float32.
+    """
+    sigma = w.sigma if sigma is None else sigma
+    std = w.weight_std
+    L, d, f, V = w.n_layers, w.d, w.ffn, w.vocab
+    model = {
+        "w_up": _as_weight(_normal((L, f, d), std, w.seed, _STREAM["w_up"]), w.wdtype),
+        "w_down": _as_weight(_normal((L, d, f), std, w.seed, _STREAM["w_down"]), w.wdtype),
+        "gain": np.ones((L + 1, d), dtype=np.float32),
+    }
+    head32 = _normal((V, d), std, w.seed, _STREAM["w_head"])
+    model["w_head"] = _as_weight(head32, w.wdtype)
+    if draft_head:
+        # The draft head is built from the *stored* target head (after bf16
+        # rounding) plus the perturbation, then rounded to the weight dtype.
+        base = head32 if w.wdtype == "f32" else bf16_bits_to_f32(model["w_head"])
+        e = _normal((V, d), std, w.seed, _STREAM["e_head"])
+        e *= np.float32(sigma)
+        e += base
+        model["w_draft_head"] = _as_weight(e, w.wdtype)
+    return model
+
+
+def make_hidden(w: Workload, M: int | None = None, sub: int = 0) -> np.ndarray:
+    """Hidden-state inputs [M, d], fp32 N(0, 1)."""
+    M = w.M if M is None else M
+    return _normal((M, w.d), 1.0, w.seed, _STREAM["hidden"], sub)
+
+
+def make_synthetic_logits(B: int, K: int, V: int, scale: float, sigma: float,
+                          seed: int = 0, sub: int = 0):
+    """Logit-space stand-ins for the accept stage alone.
+
+    target [B, K+1, V] ~ N(0, scale^2); draft [B, K, V] = target[:, :K] +
+    sigma * scale * N(0, 1).  ``scale`` mimics the spread of a normed head's
+    logits (about sqrt(d) * std(W_head)), ``sigma`` the draft head's offset.
+    """
+    t = _normal((B, K + 1, V), scale, seed, _STREAM["logits_t"], sub)
+    n = _normal((B, K, V), sigma * scale, seed, _STREAM["logits_noise"], sub)
+    n += t[:, :K, :]
+    return t, n
+
+
+def make_random_tokens(B: int, K: int, V: int, seed: int = 0, sub: int = 0) -> np.ndarray:
+    """Uniform token ids [B, K] int32 (used where any valid draft will do)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _STREAM["tokens"], sub])))
+    return g.integers(0, V, size=(B, K), dtype=np.int32)

@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verification step on one MI355X.
+
+One step = spec_verify_step over one batch: the target forward over all
+B*(K+1) positions (weights streamed once) plus rejection sampling.  Inputs
+(weights, hidden states, draft logits, draft tokens) are synthetic and
+resident in HBM before timing starts; the step is replayed from a HIP graph.
+
+Prints ONE JSON line.  Default workload: the 8B-shaped stack at B=1, K=4
+(d=4096, ffn=14336, L=8, V=32000, bf16, sigma=0.3, T=1).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
+                    [--no-cpu-baseline] [--sweep]
+
+``--sweep`` instead prints one JSON line per (B, K, sigma) point of the
+8B-shaped stack (B in 1,4,16,64; K in 1,2,4,8; sigma in 0.1, 0.5) plus the
+forward-only K=0 points, to locate the HBM -> MFMA crossover in B*(K+1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workload  # noqa: E402
+
+METRIC = "verified positions/sec + accepted tokens/sec vs B,K; % HBM / % MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16
+VALU_F32_PEAK_TFS = 157.3
+
+
+def roofline_time_s(bytes_, flops, bw=HBM_PEAK_GBS * 1e9, peak=MFMA_BF16_PEAK_TFS * 1e12):
+    """Lower bound on a step's time: max(bytes / bandwidth, flops / peak)."""
+    return max(bytes_ / bw, flops / peak)
+
+
+def step_work(w: workload.Workload, B: int, K: int, T: float):
+    """Algorithmic bytes and flops of one verification step.
+
+    bytes: weights once + hidden in + logits written once and read once +
+    draft logits read once + up to two vocab rows per request for the
+    replacement draw; flops: 2 * M * (weights' multiply-adds)."""
+    M = B * (K + 1)
+    es = 2 if w.wdtype == "bf16" else 4
+    weights = w.weight_elems() * es + (w.n_layers + 1) * w.d * 4
+    logits = M * w.vocab * 4
+    draft = 0 if T == 0 else B * K * w.vocab * 4
+    resid = 0 if T == 0 else B * 2 * w.vocab * 4
+    bytes_ = weights + M * w.d * 4 + 2 * logits + draft + resid
+    flops = 2.0 * M * w.weight_elems()
+    return bytes_, flops
+
+
+def _device_inputs(w, B, K, T, sigma, seed=0):
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    model = workload.make_model(w, sigma=sigma)
+    d_up, d_down, d_gain = dev(model["w_up"]), dev(model["w_down"]), dev(model["gain"])
+    d_head, d_dhead = dev(model["w_head"]), dev(model["w_draft_head"])
+    host = {k: model[k] for k in ("w_up", "w_down", "gain", "w_head")}
+    del model
+    M = B * (K + 1)
+    hidden = dev(workload.make_hidden(w, M))
+    target = sv.Model(d_up, d_down, d_gain, d_head)
+    # draft logits: the draft head reads the target's own final hidden state
+    drafter = sv.Model(d_up, d_down, d_gain, d_dhead)
+    zq = drafter.forward(hidden).view(B, K + 1, w.vocab)[:, :K].contiguous()
+    if T == 0:
+        x = zq.argmax(-1).to(torch.int32)
+    else:
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        u = torch.rand(zq.shape, generator=gen, device="cuda").clamp_(1e-20, 1.0)
+        x = (zq / T - torch.log(-torch.log(u))).argmax(-1).to(torch.int32)
+    del drafter, d_dhead
+    torch.cuda.synchronize()
+    return target, hidden, zq, x.contiguous(), host
+
+
+def _time_step(sv, target, hidden, zq, x, B, K, T, steps, warmup, use_graph, seed=0, stp=0):
+    import torch
+    M = B * (K + 1)
+    V = target.vocab
+    ws = sv.workspace(target.workspace_bytes(B, K))
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+
+    def one():
+        target.step(hidden, zq if T > 0 else None, x, B, K, T, seed, stp, logits, out, al,
+                    ws=ws, stream=s)
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(warmup, 1)):
+            one()
+    torch.cuda.synchronize()
+    g = None
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                one()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                g.replay()
+        torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        start.record(s)
+        for i in range(steps):
+            if g is not None:
+                g.replay()
+            else:
+                one()
+        stop.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    # per-step spread from a second, individually-timed pass (not the headline)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(steps, 50))]
+    with torch.cuda.stream(s):
+        for a, b in evs:
+            a.record(s)
+            g.replay() if g is not None else one()
+            b.record(s)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return ms, wall, per, (logits, out, al, ws, s, one)
+
+
+def _profile_kernels(sv, one, s, reps):
+    import torch
+    sv.profile_begin(1 << 16)
+    with torch.cuda.stream(s):
+        for _ in range(reps):
+            one()
+    torch.cuda.synchronize()
+    return sv.profile_end(64)
+
+
+def _cpu_baseline(host, w, B, K, T, seed, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    from oracle import forward as of, verify as ov
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    nreq = 1
+    rows = list(range(nreq * (K + 1)))
+    hidden = workload.make_hidden(w, B * (K + 1))[rows]
+    g = np.random.default_rng(seed)
+    zd = g.standard_normal((nreq, K, w.vocab)) * math.sqrt(w.d) * w.weight_std
+    x = ov.sample_draft_tokens(zd, T, seed, 0)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        z = of.forward(host, hidden)
+        ov.verify(z.reshape(nreq, K + 1, w.vocab), zd, x, T, seed, n)
+        n += 1
+        if time.perf_counter() - t0 > budget_s / 2 or n >= 3:
+            break
+    el = time.perf_counter() - t0
+    return {"value": n * len(rows) / el, "unit": "verified positions/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} oracle step(s) of one request ({len(rows)} positions: fp64 forward "
+                      f"through all {w.n_layers} blocks and the head, then rejection sampling), "
+                      f"{el:.1f} s"}
+
+
+def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile=True):
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    M = B * (K + 1)
+    target, hidden, zq, x, host = _device_inputs(w, B, K, T, sigma)
+    ms, wall, per, (logits, out, al, ws, s, one) = _time_step(
+        sv, target, hidden, zq, x, B, K, T, steps, warmup, use_graph)
+    al_h = al.cpu().numpy()
+    # acceptance statistics over a few fresh uniform streams (untimed)
+    als = [al_h]
+    for stp in range(1, 8):
+        target.step(hidden, zq if T > 0 else None, x, B, K, T, 0, stp, logits, out, al, ws=ws)
+        als.append(al.cpu().numpy().copy())
+    als = np.concatenate(als)
+    bytes_, flops = step_work(w, B, K, T)
+    res = {
+        "metric": METRIC,
+        "value": M / (ms / 1e3),
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.wdtype == "bf16" else "f32",
+        "data": "synthetic (seeded random weights and inputs of the stated shapes)",
+        "config": {"workload": w.name, "B": B, "K": K, "M": M, "d": w.d, "ffn": w.ffn,
+                   "n_layers": w.n_layers, "vocab": w.vocab, "sigma": sigma, "temperature": T,
+                   "launch": "hipgraph" if use_graph else "eager", "parallelism": "none (1 GPU)"},
+        "accepted_tokens_per_s": float(al_h.sum()) / (ms / 1e3),
+        "mean_accept_len": float(als.mean()),
+        "accept_len_hist": np.bincount(als, minlength=K + 2)[1:].tolist(),
+        "step_ms_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2], per[(9 * len(per)) // 10]],
+        "wall_s_timed": wall,
+        "step_bytes": bytes_,
+        "step_flops": flops,
+        "step_hbm_frac": bytes_ / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
+        "step_mfma_frac": flops / (ms / 1e3) / (MFMA_BF16_PEAK_TFS * 1e12),
+        "roofline_step_ms": roofline_time_s(bytes_, flops) * 1e3,
+    }
+    if profile:
+        kt = _profile_kernels(sv, one, s, reps=5)
+        dom = max(kt, key=lambda k: kt[k][1])
+        n, tot, b, f = kt[dom]
+        avg_s = tot / n / 1e3
+        mem_bound = (f / max(b, 1)) < (MFMA_BF16_PEAK_TFS / HBM_PEAK_GBS * 1e3)
+        if mem_bound or w.wdtype != "bf16":
+            roof = {"bound": "hbm", "achieved": b / n / avg_s / 1e9, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": f / n / avg_s / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        roof["kernel"] = dom
+        roof["avg_launch_us"] = avg_s * 1e6
+        roof["algorithmic_bytes_per_launch"] = b / n
+        roof["algorithmic_flops_per_launch"] = f / n
+        res["roofline"] = roof
+        res["kernels"] = {k: {"launches": v[0] // 5, "ms_per_step": v[1] / 5,
+                              "gbs": v[2] / max(v[1], 1e-9) / 1e6} for k, v in kt.items()}
+    if cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline(host, w, B, K, T, 0)
+    del target, hidden, zq, x, logits, out, al, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="8b-shaped-b1-k4", choices=sorted(workload.WORKLOADS))
+    ap.add_argument("--B", type=int)
+    ap.add_argument("--K", type=int)
+    ap.add_argument("--sigma", type=float)
+    ap.add_argument("--T", type=float)
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(the step is data-parallel over requests; see the design notes for sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if a.sweep:
+        w = workload.WORKLOADS["8b-shaped-sweep"]
+        for sigma in workload.SWEEP_SIGMA:
+            for B in workload.SWEEP_B:
+                for K in workload.SWEEP_K:
+                    r = run_point(w, B, K, sigma, 1.0, max(20, a.steps // 4), 3, not a.eager,
+                                  False, profile=False)
+                    print(json.dumps(r), flush=True)
+        return
+
+    w = workload.WORKLOADS[a.workload]
+    B = a.B or w.B
+    K = w.K if a.K is None else a.K
+    sigma = w.sigma if a.sigma is None else a.sigma
+    T = w.temperature if a.T is None else a.T
+    res = run_point(w, B, K, sigma, T, a.steps, a.warmup, not a.eager, not a.no_cpu_baseline,
+                    profile=not a.no_profile)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,6 +16,13 @@ rounded to bf16 (round to nearest even) when the weights are bf16, because
 the product is defined as bf16 inputs with fp32-or-better accumulation.  With
 fp32 weights nothing is rounded.
 
+``accum="f32"`` runs the same block order with fp32 matmuls (BLAS sgemm) and
+the same bf16 rounding points.  It exists only to measure how far two valid
+accumulation orders of this contract drift apart through the stack (each
+bf16 rounding decision can flip when the pre-rounding value moves by one
+fp32 rounding, and a random MLP stack amplifies the flips layer by layer);
+comparisons against the GPU use the fp64 default.
+
 Pinned by: torch.nn.functional (rms_norm, silu, linear) in float64 composed
 in the same block order; special cases (zero down weights leave h unchanged;
 zero layers reduce to the head on norm(hidden)); RMSNorm's scale invariance;
@@ -37,13 +44,14 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # np.rint: ties to even
 
 
-def weights_f64(w: np.ndarray, lo: int | None = None, hi: int | None = None) -> np.ndarray:
+def weights_f64(w: np.ndarray, lo: int | None = None, hi: int | None = None,
+                dtype=np.float64) -> np.ndarray:
     """Rows [lo, hi) of a stored weight matrix as fp64 (bf16 patterns are
     uint16; fp32 matrices pass through).  The upcast is exact."""
     part = w[lo:hi]
     if part.dtype == np.uint16:
-        return (part.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return part.astype(np.float64)
+        return (part.astype(np.uint32) << 16).view(np.float32).astype(dtype)
+    return part.astype(dtype)
 
 
 def rmsnorm(h: np.ndarray, g: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
@@ -56,32 +64,49 @@ def silu(u: np.ndarray) -> np.ndarray:
     return u / (1.0 + np.exp(-u))
 
 
-def head(a_f: np.ndarray, w_head: np.ndarray) -> np.ndarray:
+_ACCUM = {"f64": np.float64, "f32": np.float32}
+
+
+def head(a_f: np.ndarray, w_head: np.ndarray, accum: str = "f64") -> np.ndarray:
     """Logits a_f . W_head^T, taking the head in row blocks to bound memory."""
+    dt = _ACCUM[accum]
     V = w_head.shape[0]
     out = np.empty((a_f.shape[0], V), dtype=np.float64)
+    a = a_f.astype(dt)
     for lo in range(0, V, _HEAD_ROWS):
         hi = min(lo + _HEAD_ROWS, V)
-        out[:, lo:hi] = a_f @ weights_f64(w_head, lo, hi).T
+        out[:, lo:hi] = a @ weights_f64(w_head, lo, hi, dt).T
     return out
 
 
-def final_activation(model: dict, hidden: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+def final_activation(model: dict, hidden: np.ndarray, eps: float = RMS_EPS,
+                     accum: str = "f64") -> np.ndarray:
     """Run the L blocks and the final norm; returns a_f [rows, d] (fp64)."""
+    dt = _ACCUM[accum]
     rnd = bf16_round if model["w_up"].dtype == np.uint16 else (lambda v: v)
     h = np.asarray(hidden, dtype=np.float64)
     g = np.asarray(model["gain"], dtype=np.float64)
     L = model["w_up"].shape[0]
     for l in range(L):
-        a = rnd(rmsnorm(h, g[l], eps))
-        s = rnd(silu(a @ weights_f64(model["w_up"][l]).T))
-        h = h + s @ weights_f64(model["w_down"][l]).T
+        a = rnd(rmsnorm(h, g[l], eps)).astype(dt)
+        s = rnd(silu((a @ weights_f64(model["w_up"][l], dtype=dt).T).astype(np.float64))).astype(dt)
+        h = h + (s @ weights_f64(model["w_down"][l], dtype=dt).T).astype(np.float64)
     return rnd(rmsnorm(h, g[L], eps))
 
 
-def forward(model: dict, hidden: np.ndarray, heads=("w_head",), eps: float = RMS_EPS):
+def forward(model: dict, hidden: np.ndarray, heads=("w_head",), eps: float = RMS_EPS,
+            accum: str = "f64"):
     """Logits [rows, V] (fp64) for each requested head of ``model``.
     Returns one array, or a tuple when several heads are asked for."""
-    a_f = final_activation(model, hidden, eps)
-    outs = tuple(head(a_f, model[name]) for name in heads)
+    a_f = final_activation(model, hidden, eps, accum)
+    outs = tuple(head(a_f, model[name], accum) for name in heads)
     return outs[0] if len(outs) == 1 else outs
+
+
+def truncated(model: dict, n_layers: int) -> dict:
+    """The first n_layers blocks of ``model`` with its final norm and heads."""
+    out = dict(model)
+    out["w_up"] = model["w_up"][:n_layers]
+    out["w_down"] = model["w_down"][:n_layers]
+    out["gain"] = np.concatenate([model["gain"][:n_layers], model["gain"][-1:]])
+    return out

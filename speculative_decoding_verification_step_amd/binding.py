@@ -1,0 +1,244 @@
+"""ctypes binding of libspecverify.so (include/spec_verify.h).
+
+Argument marshalling only: torch is used for device memory and the current
+HIP stream; every step of the verification runs in the library's kernels.
+The library must have been built in-tree; nothing falls back to Python or
+CPU code when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
+SV_F32, SV_BF16 = 0, 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_u64 = ctypes.c_uint64
+_sz = ctypes.c_size_t
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"spec_verify error {code}: {msg}")
+        self.code = code
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("d", _i32), ("ffn", _i32), ("n_layers", _i32), ("vocab", _i32),
+                ("wdtype", _i32), ("rms_eps", ctypes.c_float),
+                ("w_up", _vp), ("w_down", _vp), ("gain", _vp), ("w_head", _vp)]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", _i32), ("total_ms", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
+
+
+EXPORTS = {
+    "spec_verify_abi_version": (_i32, []),
+    "sv_model_create": (ctypes.c_int, [ctypes.POINTER(ModelDesc), ctypes.POINTER(_vp)]),
+    "sv_model_destroy": (None, [_vp]),
+    "spec_verify_forward_workspace_bytes": (_sz, [_vp, _i32]),
+    "spec_verify_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "spec_verify_workspace_bytes": (_sz, [_vp, _i32, _i32]),
+    "spec_verify_forward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "spec_verify_accept": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float, _u64,
+                                          _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _u64, _u32,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_last_error": (ctypes.c_char_p, []),
+    "spec_verify_profile_begin": (ctypes.c_int, [_i32]),
+    "spec_verify_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), _i32,
+                                               ctypes.POINTER(_i32)]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first with "
+                "`python -m speculative_decoding_verification_step_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, lib().spec_verify_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A caller-owned workspace buffer (256-byte aligned by torch's allocator)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device or "cuda")
+
+
+class Model:
+    """Borrowed view of target weights already resident on the GPU.
+
+    w_up [L, ffn, d], w_down [L, d, ffn], w_head [V, d] (bfloat16 or float32),
+    gain [L+1, d] float32.  The tensors are kept referenced for the model's
+    lifetime."""
+
+    def __init__(self, w_up, w_down, gain, w_head, rms_eps: float = 1e-5):
+        dt = w_head.dtype
+        if dt not in (torch.bfloat16, torch.float32):
+            raise ValueError("weights must be bfloat16 or float32")
+        V, d = w_head.shape
+        L, ffn = w_up.shape[0], w_up.shape[1]
+        _need(w_up, "w_up", dt, (L, ffn, d))
+        _need(w_down, "w_down", dt, (L, d, ffn))
+        _need(gain, "gain", torch.float32, (L + 1, d))
+        _need(w_head, "w_head", dt, (V, d))
+        self._keep = (w_up, w_down, gain, w_head)
+        self.d, self.ffn, self.n_layers, self.vocab, self.dtype = d, ffn, L, V, dt
+        desc = ModelDesc(d, ffn, L, V, SV_BF16 if dt == torch.bfloat16 else SV_F32, rms_eps,
+                         w_up.data_ptr() if L else None, w_down.data_ptr() if L else None,
+                         gain.data_ptr(), w_head.data_ptr())
+        h = ctypes.c_void_p()
+        _check(lib().sv_model_create(ctypes.byref(desc), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.sv_model_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def forward_workspace_bytes(self, M: int) -> int:
+        return int(lib().spec_verify_forward_workspace_bytes(self._h, M))
+
+    def workspace_bytes(self, B: int, K: int) -> int:
+        return int(lib().spec_verify_workspace_bytes(self._h, B, K))
+
+    def forward(self, hidden, logits=None, ws=None, stream=None):
+        """Logits [M, V] fp32 of hidden [M, d] fp32."""
+        M = hidden.shape[0]
+        _need(hidden, "hidden", torch.float32, (M, self.d))
+        if logits is None:
+            logits = torch.empty((M, self.vocab), dtype=torch.float32, device=hidden.device)
+        _need(logits, "logits", torch.float32, (M, self.vocab))
+        if ws is None:
+            ws = workspace(self.forward_workspace_bytes(M), hidden.device)
+        _check(lib().spec_verify_forward(self._h, _ptr(hidden), M, _ptr(logits), _ptr(ws),
+                                         ws.numel(), _stream(stream)))
+        return logits
+
+    def step(self, hidden, draft_logits, draft_tokens, B: int, K: int, temperature: float,
+             seed: int, step: int, logits=None, out_tokens=None, accept_len=None,
+             p_at=None, q_at=None, ws=None, stream=None):
+        """The whole verification step; returns (logits, out_tokens, accept_len)."""
+        M = B * (K + 1)
+        dev = hidden.device
+        _need(hidden, "hidden", torch.float32, (M, self.d))
+        if draft_logits is not None:
+            _need(draft_logits, "draft_logits", torch.float32, (B, K, self.vocab))
+        if draft_tokens is not None:
+            _need(draft_tokens, "draft_tokens", torch.int32, (B, K))
+        if logits is None:
+            logits = torch.empty((M, self.vocab), dtype=torch.float32, device=dev)
+        if out_tokens is None:
+            out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        if accept_len is None:
+            accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        _need(logits, "logits", torch.float32, (M, self.vocab))
+        _need(out_tokens, "out_tokens", torch.int32, (B, K + 1))
+        _need(accept_len, "accept_len", torch.int32, (B,))
+        for t, n in ((p_at, "p_at"), (q_at, "q_at")):
+            if t is not None:
+                _need(t, n, torch.float32, (B, K))
+        if ws is None:
+            ws = workspace(self.workspace_bytes(B, K), dev)
+        _check(lib().spec_verify_step(self._h, _ptr(hidden), _ptr(draft_logits), _ptr(draft_tokens),
+                                      B, K, float(temperature), int(seed), int(step), _ptr(logits),
+                                      _ptr(out_tokens), _ptr(accept_len), _ptr(p_at), _ptr(q_at),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+        return logits, out_tokens, accept_len
+
+
+def accept_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(lib().spec_verify_accept_workspace_bytes(B, K, V))
+
+
+def accept(target_logits, draft_logits, draft_tokens, temperature: float, seed: int, step: int,
+           out_tokens=None, accept_len=None, p_at=None, q_at=None, ws=None, stream=None):
+    """Rejection sampling alone: target_logits [B, K+1, V], draft_logits
+    [B, K, V] (or None at T = 0 / K = 0), draft_tokens [B, K] int32.
+    Returns (out_tokens [B, K+1], accept_len [B])."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, K1, V))
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, (B, K, V))
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(accept_workspace_bytes(B, K, V), dev)
+    _check(lib().spec_verify_accept(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+                                    B, K, V, float(temperature), int(seed), int(step),
+                                    _ptr(out_tokens), _ptr(accept_len), _ptr(p_at), _ptr(q_at),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return out_tokens, accept_len
+
+
+def profile_begin(max_launches: int = 65536):
+    _check(lib().spec_verify_profile_begin(max_launches))
+
+
+def profile_end(cap: int = 64):
+    """Stop per-launch timing; returns {name: (launches, total_ms, bytes, flops)}."""
+    arr = (KernelTime * cap)()
+    n = _i32(0)
+    _check(lib().spec_verify_profile_end(arr, cap, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms, arr[i].bytes, arr[i].flops)
+            for i in range(min(n.value, cap))}

@@ -1,0 +1,68 @@
+// Internal launchers of the verification-step kernels.  Host code only sees
+// these declarations; every launcher enqueues on `stream` and returns the
+// launch status (hipGetLastError after the launch).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+// Epilogue of a weight-streaming matmul  out[m, n] = sum_k act[m, k] * W[n, k].
+enum Epi : int {
+    kEpiSilu = 0,      // act_out[m, n] = round_act(silu(acc))         (up projection)
+    kEpiResidual = 1,  // h[m, n] += acc  (fp32; one owner per element)  (down projection)
+    kEpiStore = 2,     // f32_out[m, n] = acc                          (LM head)
+};
+
+struct MatmulArgs {
+    const void* W;        // [N, K] weights (bf16 bits or fp32)
+    const void* act;      // [M, K] activations, same dtype as W
+    int M, N, K;
+    int epi;
+    void* out;            // act_out (kEpiSilu), h (kEpiResidual) or f32_out (kEpiStore)
+    int bf16;             // 1: bf16 weights/activations, 0: fp32
+};
+
+// Kernel families a matmul can run on.
+enum MatmulKind : int {
+    kGemvValu = 0,        // VALU dot products, M <= 8 per launch (m-chunks above)
+    kMfmaSkinny = 1,      // bf16 MFMA, weights streamed straight to registers
+    kMfmaTiled = 2,       // bf16 MFMA, LDS-staged tiles for large M
+};
+
+hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream);
+
+// RMSNorm of each row:  act = round_act(h / sqrt(mean(h^2) + eps) * gain)
+// with h = src; when hout != src the row is also copied to hout (the first
+// block copies the caller's hidden states into the residual stream).
+hipError_t launch_rmsnorm(const float* src, float* hout, const float* gain, void* act, int M,
+                          int d, float eps, int bf16, hipStream_t stream);
+
+// Softmax statistics at temperature T (1/T = inv_t), per chunk of
+// stats_chunks(V) chunks of each row: chunk max and sum of exp((z - max) / T)
+// into pv/ps [rows, nchunk]; at T = 0 the chunk max and argmax (lowest id on
+// ties) into pv/pi.  Rows 0..n_t-1 come from `target`, n_t.. from `draft`.
+int stats_chunks(int V);
+hipError_t launch_row_stats(const float* target, const float* draft, int n_t, int n_d, int V,
+                            float inv_t, int greedy, float* pv, float* ps, int* pi,
+                            hipStream_t stream);
+
+// Accept / resample / bonus for B requests (one workgroup each), folding the
+// chunk statistics written by launch_row_stats.
+hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens, int B,
+                         int K, int V, float inv_t, int greedy, uint64_t seed, uint32_t step,
+                         const float* pv, const float* ps, const int* pi, int32_t* out_tokens,
+                         int32_t* accept_len, float* p_at, float* q_at, hipStream_t stream);
+
+// Per-launch timing hook (implemented by the host layer): brackets one
+// launch with events when profiling is on.
+struct ProfScope {
+    ProfScope(const char* name, hipStream_t s, double bytes, double flops);
+    ~ProfScope();
+    int slot;
+    hipStream_t stream;
+};
+
+}  // namespace sv

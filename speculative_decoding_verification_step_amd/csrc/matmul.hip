@@ -1,0 +1,42 @@
+// Dispatch of the weight-streaming matmuls to a kernel family, with the
+// per-launch timing scope (algorithmic bytes and flops of the launch).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sv {
+
+hipError_t launch_gemv(const MatmulArgs& a, hipStream_t stream);
+hipError_t launch_mfma_skinny(const MatmulArgs& a, hipStream_t stream);
+hipError_t launch_mfma_tiled(const MatmulArgs& a, hipStream_t stream);
+
+namespace {
+
+const char* scope_name(int kind, int epi) {
+    static const char* names[3][3] = {
+        {"gemv_valu.up_silu", "gemv_valu.down_residual", "gemv_valu.head"},
+        {"mfma_skinny.up_silu", "mfma_skinny.down_residual", "mfma_skinny.head"},
+        {"mfma_tiled.up_silu", "mfma_tiled.down_residual", "mfma_tiled.head"},
+    };
+    return names[kind][epi];
+}
+
+}  // namespace
+
+hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream) {
+    if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    if (kind < 0 || kind > 2 || a.epi < 0 || a.epi > 2) return hipErrorInvalidValue;
+    const double es = a.bf16 ? 2.0 : 4.0;
+    const double out_es = a.epi == kEpiSilu ? es : 4.0;
+    // weights + activations + outputs (the residual is read and written)
+    const double bytes = (double)a.N * a.K * es + (double)a.M * a.K * es +
+                         (double)a.M * a.N * out_es * (a.epi == kEpiResidual ? 2 : 1);
+    const double flops = 2.0 * a.M * (double)a.N * a.K;
+    ProfScope prof(scope_name(kind, a.epi), stream, bytes, flops);
+    switch (kind) {
+        case kGemvValu: return launch_gemv(a, stream);
+        case kMfmaSkinny: return launch_mfma_skinny(a, stream);
+        default: return launch_mfma_tiled(a, stream);
+    }
+}
+
+}  // namespace sv

@@ -1,0 +1,107 @@
+// RMSNorm of the residual stream before every block and before the LM head.
+//
+// The pre-norm residual block of the synthetic target:
+// a = round_act(h / sqrt(mean(h^2) + eps) * g).  One workgroup owns one row;
+// every thread holds its VPT float4 vectors of the row in registers, so all of
+// the row's loads are in flight at once, and the sum of squares is reduced
+// inside the workgroup in a fixed order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sv {
+
+namespace {
+
+template <bool kBf16, int VPT, int THREADS>
+__global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
+    const float* src, float* hout,  // src may equal hout (then nothing is copied)
+    const float* __restrict__ gain, void* __restrict__ act, int d, float eps) {
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const size_t off = (size_t)row * d;
+    const int n4 = d >> 2;
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src + off);
+
+    f32x4 h[VPT];
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = tid + v * THREADS;
+        h[v] = c < n4 ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        ss += h[v].x * h[v].x;
+        ss += h[v].y * h[v].y;
+        ss += h[v].z * h[v].z;
+        ss += h[v].w * h[v].w;
+    }
+    if (hout != src) {
+        f32x4* h4 = reinterpret_cast<f32x4*>(hout + off);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = tid + v * THREADS;
+            if (c < n4) h4[c] = h[v];
+        }
+    }
+
+    __shared__ float red[THREADS / kWave];
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < THREADS / kWave; ++w) tot += red[w];
+    const float inv_rms = 1.0f / sqrtf(tot / (float)d + eps);
+
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(gain);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = tid + v * THREADS;
+        if (c >= n4) continue;
+        const f32x4 g = g4[c];
+        const f32x4 y = {h[v].x * inv_rms * g.x, h[v].y * inv_rms * g.y, h[v].z * inv_rms * g.z,
+                         h[v].w * inv_rms * g.w};
+        if constexpr (kBf16) {
+            uint2 packed;
+            packed.x = f32_to_bf16(y.x) | (f32_to_bf16(y.y) << 16);
+            packed.y = f32_to_bf16(y.z) | (f32_to_bf16(y.w) << 16);
+            reinterpret_cast<uint2*>(static_cast<uint16_t*>(act) + off)[c] = packed;
+        } else {
+            reinterpret_cast<f32x4*>(static_cast<float*>(act) + off)[c] = y;
+        }
+    }
+}
+
+template <bool kBf16>
+hipError_t launch_norm_dtype(const float* src, float* hout, const float* gain, void* act, int M,
+                             int d, float eps, hipStream_t stream) {
+    const int n4 = d / 4;
+    if (n4 <= 256) {
+        rmsnorm_kernel<kBf16, 1, 256><<<M, 256, 0, stream>>>(src, hout, gain, act, d, eps);
+    } else if (n4 <= 1024) {
+        rmsnorm_kernel<kBf16, 1, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+    } else if (n4 <= 2048) {
+        rmsnorm_kernel<kBf16, 2, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+    } else if (n4 <= 4096) {
+        rmsnorm_kernel<kBf16, 4, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+    } else if (n4 <= 8192) {
+        rmsnorm_kernel<kBf16, 8, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const float* src, float* hout, const float* gain, void* act, int M,
+                          int d, float eps, int bf16, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    const double bytes = (double)M * d * (4.0 + (hout != src ? 4.0 : 0.0) + (bf16 ? 2.0 : 4.0));
+    ProfScope prof("rmsnorm", stream, bytes, 0.0);
+    return bf16 ? launch_norm_dtype<true>(src, hout, gain, act, M, d, eps, stream)
+                : launch_norm_dtype<false>(src, hout, gain, act, M, d, eps, stream);
+}
+
+}  // namespace sv

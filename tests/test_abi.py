@@ -1,0 +1,164 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_decoding_verification_step_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+FAKE = 0x10000  # a non-null, aligned address; never dereferenced by the host checks
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("libspecverify.so not built")
+    return bd.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("spec_verify_forward", "spec_verify_accept", "spec_verify_step",
+              "sv_model_create", "sv_model_destroy", "spec_verify_workspace_bytes",
+              "spec_verify_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    assert set(bd.EXPORTS) <= exported
+
+
+def test_abi_version(L):
+    assert L.spec_verify_abi_version() == 1
+
+
+def _desc(**kw):
+    base = dict(d=256, ffn=1024, n_layers=2, vocab=4096, wdtype=bd.SV_BF16, rms_eps=1e-5,
+                w_up=FAKE, w_down=FAKE, gain=FAKE, w_head=FAKE)
+    base.update(kw)
+    return bd.ModelDesc(base["d"], base["ffn"], base["n_layers"], base["vocab"], base["wdtype"],
+                        base["rms_eps"], base["w_up"], base["w_down"], base["gain"], base["w_head"])
+
+
+def _create(L, **kw):
+    h = ctypes.c_void_p()
+    rc = L.sv_model_create(ctypes.byref(_desc(**kw)), ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=0), bd.SV_ERR_INVALID_ARG), (dict(vocab=0), bd.SV_ERR_INVALID_ARG),
+    (dict(n_layers=-1), bd.SV_ERR_INVALID_ARG), (dict(d=100), bd.SV_ERR_UNSUPPORTED), (dict(d=32832), bd.SV_ERR_UNSUPPORTED),
+    (dict(ffn=1000), bd.SV_ERR_UNSUPPORTED), (dict(wdtype=7), bd.SV_ERR_UNSUPPORTED),
+    (dict(rms_eps=-1.0), bd.SV_ERR_INVALID_ARG), (dict(rms_eps=float("nan")), bd.SV_ERR_INVALID_ARG),
+    (dict(w_head=0), bd.SV_ERR_INVALID_ARG), (dict(w_up=FAKE + 4), bd.SV_ERR_INVALID_ARG),
+])
+def test_model_create_rejects(L, kw, code):
+    rc, h = _create(L, **kw)
+    assert rc == code and not h.value
+    assert L.spec_verify_last_error()
+
+
+def test_model_create_zero_layers_allows_null_blocks(L):
+    rc, h = _create(L, n_layers=0, w_up=0, w_down=0)
+    assert rc == 0 and h.value
+    L.sv_model_destroy(h)
+
+
+def test_workspace_sizes(L):
+    rc, h = _create(L)
+    assert rc == 0
+    try:
+        f = L.spec_verify_forward_workspace_bytes(h, 5)
+        a = L.spec_verify_accept_workspace_bytes(1, 4, 4096)
+        s = L.spec_verify_workspace_bytes(h, 1, 4)
+        assert f > 0 and a > 0 and s == f + a
+        assert f % 256 == 0 and a % 256 == 0
+        assert L.spec_verify_forward_workspace_bytes(h, -1) == 0
+        assert L.spec_verify_workspace_bytes(None, 1, 4) == 0
+        # grows with the number of rows
+        assert L.spec_verify_forward_workspace_bytes(h, 40) > f
+    finally:
+        L.sv_model_destroy(h)
+
+
+def _accept(L, B=1, K=4, V=4096, T=1.0, tl=FAKE, dl=FAKE, x=FAKE, out=FAKE, al=FAKE, ws=FAKE,
+            ws_bytes=1 << 20):
+    return L.spec_verify_accept(tl, dl, x, B, K, V, T, 0, 0, out, al, None, None, ws, ws_bytes,
+                                None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), bd.SV_ERR_INVALID_ARG), (dict(K=-1), bd.SV_ERR_INVALID_ARG),
+    (dict(V=0), bd.SV_ERR_INVALID_ARG), (dict(T=-1.0), bd.SV_ERR_INVALID_ARG),
+    (dict(T=float("nan")), bd.SV_ERR_INVALID_ARG), (dict(T=float("inf")), bd.SV_ERR_INVALID_ARG),
+    (dict(T=1e-40), bd.SV_ERR_INVALID_ARG), (dict(tl=0), bd.SV_ERR_INVALID_ARG),
+    (dict(x=0), bd.SV_ERR_INVALID_ARG), (dict(dl=0), bd.SV_ERR_INVALID_ARG),
+    (dict(out=0), bd.SV_ERR_INVALID_ARG), (dict(al=0), bd.SV_ERR_INVALID_ARG),
+    (dict(ws=0), bd.SV_ERR_WORKSPACE), (dict(ws_bytes=16), bd.SV_ERR_WORKSPACE),
+    (dict(ws=FAKE + 64), bd.SV_ERR_WORKSPACE),
+])
+def test_accept_rejects(L, kw, code):
+    assert _accept(L, **kw) == code
+    assert L.spec_verify_last_error()
+
+
+def test_accept_allows_null_draft_when_greedy_or_k0(L):
+    # these pass the host checks; B = 0 keeps them from launching anything
+    assert _accept(L, B=0, T=0.0, dl=0) == 0
+    assert _accept(L, B=0, K=0, dl=0, x=0) == 0
+
+
+def test_empty_batch_is_noop(L):
+    assert _accept(L, B=0, tl=0, dl=0, x=0, out=0, al=0, ws=0, ws_bytes=0) == 0
+    rc, h = _create(L)
+    try:
+        assert L.spec_verify_forward(h, None, 0, None, None, 0, None) == 0
+        assert L.spec_verify_step(h, None, None, None, 0, 4, 1.0, 0, 0, None, None, None, None,
+                                  None, None, 0, None) == 0
+    finally:
+        L.sv_model_destroy(h)
+
+
+def test_forward_and_step_reject(L):
+    rc, h = _create(L)
+    try:
+        need = L.spec_verify_forward_workspace_bytes(h, 5)
+        fw = L.spec_verify_forward
+        assert fw(None, FAKE, 5, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert fw(h, FAKE, -1, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert fw(h, 0, 5, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert fw(h, FAKE + 4, 5, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert fw(h, FAKE, 5, FAKE, FAKE, need - 1, None) == bd.SV_ERR_WORKSPACE
+        st = L.spec_verify_step
+        need = L.spec_verify_workspace_bytes(h, 1, 4)
+        assert st(h, FAKE, FAKE, FAKE, 1, 4, -2.0, 0, 0, FAKE, FAKE, FAKE, None, None, FAKE, need,
+                  None) == bd.SV_ERR_INVALID_ARG
+        assert st(h, FAKE, FAKE, FAKE, 1, 4, 1.0, 0, 0, FAKE, FAKE, FAKE, None, None, FAKE,
+                  need - 256, None) == bd.SV_ERR_WORKSPACE
+        assert st(h, 0, FAKE, FAKE, 1, 4, 1.0, 0, 0, FAKE, FAKE, FAKE, None, None, FAKE, need,
+                  None) == bd.SV_ERR_INVALID_ARG
+    finally:
+        L.sv_model_destroy(h)
+
+
+def test_profile_state_machine(L):
+    assert L.spec_verify_profile_end(None, 0, None) == bd.SV_ERR_INVALID_ARG
+    assert L.spec_verify_profile_begin(0) == bd.SV_ERR_INVALID_ARG

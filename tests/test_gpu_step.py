@@ -1,0 +1,121 @@
+"""GPU parity of the whole verification step (spec_verify_step).
+
+Inputs: target weights and hidden states from ``workload``; draft logits and
+draft tokens from the oracle (the draft head reads the target's final hidden
+state).  The GPU step computes its own target logits, which differ from the
+oracle's by the forward tolerance; a request is compared bit for bit unless
+its oracle decisions lie within the band that the measured logit difference
+can move (derived in tests/gpu_helpers.step_band_near).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workload
+from oracle import forward as of, verify as ov
+from tests.gpu_helpers import (compare_accept, cpu, device_model, full_stack_tol, gpu,
+                               host_workload, note, require_gpu, step_band_near)
+
+
+def _step_case(name, requests, T=None, step=0, seed=0):
+    sv = require_gpu()
+    w = workload.WORKLOADS[name]
+    T = w.temperature if T is None else T
+    B, K, V = w.B, w.K, w.vocab
+    model, hidden = host_workload(name)
+    rows = [b * (K + 1) + j for b in requests for j in range(K + 1)]
+    note(f"{name}: oracle forward on requests {requests}")
+    zt_ref, zd_ref = of.forward(model, hidden[rows], heads=("w_head", "w_draft_head"))
+    zt_ref = zt_ref.reshape(len(requests), K + 1, V)
+    zd_ref = zd_ref.reshape(len(requests), K + 1, V)[:, :K]
+    # draft inputs: oracle values for the checked requests, plain filler elsewhere
+    dl = np.zeros((B, K, V), np.float32)
+    dl[requests] = zd_ref.astype(np.float32)
+    x = workload.make_random_tokens(B, K, V, seed=seed)
+    x[requests] = ov.sample_draft_tokens(dl[requests], T, seed, step)
+
+    m = device_model(sv, model)
+    logits, out, al = m.step(torch.from_numpy(hidden).cuda(), torch.from_numpy(dl).cuda(),
+                             torch.from_numpy(x).cuda(), B, K, T, seed, step)
+    torch.cuda.synchronize()
+    z_gpu = cpu(logits).reshape(B, K + 1, V)
+    out, al = cpu(out), cpu(al)
+    assert np.all((al >= 1) & (al <= K + 1))
+
+    tl_ref = np.zeros((B, K + 1, V))
+    tl_ref[requests] = zt_ref
+    dl_ref = dl.astype(np.float64)
+    ref_out, ref_al, res = ov.verify(tl_ref, dl_ref, x, T, seed, step, requests=requests)
+    set_aside = 0
+    for i, b in enumerate(requests):
+        eps = float(np.max(np.abs(z_gpu[b] - zt_ref[i])))
+        assert eps <= full_stack_tol(name), f"logits of request {b} off by {eps}"
+        if step_band_near(res[b], eps, T, zt_ref[i]):
+            set_aside += 1
+            continue
+        compare_accept(out, al, ref_out, ref_al, res, requests=[b])
+    note(f"{name}: {len(requests) - set_aside}/{len(requests)} requests bit-exact, "
+         f"{set_aside} inside the band; AL = {al[requests].tolist()}")
+    return al
+
+
+@gpu
+def test_tiny_fp32_step():
+    _step_case("tiny-fp32", [0])
+    for s in range(1, 6):
+        _step_case("tiny-fp32", [0], step=s)
+
+
+@gpu
+def test_8b_shaped_b1k4_step():
+    _step_case("8b-shaped-b1-k4", [0])
+
+
+@gpu
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_70b_share_step(T):
+    _step_case("70b-layer-share-b8-k4", [0, 3, 7], T=T)
+
+
+@gpu
+def test_large_batch_step():
+    _step_case("large-batch-b256-k2", [0, 128, 255])
+
+
+@gpu
+def test_step_graph_replay_matches_eager():
+    """A captured step replays to the eager result, with eager work and
+    synchronisation between replays."""
+    sv = require_gpu()
+    w = workload.Workload("graph", 512, 1024, 2, 5000, "bf16", 4, 3, 0.3, 1.0, "std_0.02", 3)
+    model = workload.make_model(w)
+    hidden = torch.from_numpy(workload.make_hidden(w)).cuda()
+    zt, zd = of.forward(model, workload.make_hidden(w), heads=("w_head", "w_draft_head"))
+    B, K, V = w.B, w.K, w.vocab
+    dl = zd.reshape(B, K + 1, V)[:, :K].astype(np.float32)
+    x = ov.sample_draft_tokens(dl, 1.0, 0, 0)
+    m = device_model(sv, model)
+    dl_t, x_t = torch.from_numpy(dl).cuda(), torch.from_numpy(x).cuda()
+    ws = sv.workspace(m.workspace_bytes(B, K))
+    logits = torch.empty((B * (K + 1), V), device="cuda")
+    out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    m.step(hidden, dl_t, x_t, B, K, 1.0, 0, 0, logits, out, al, ws=ws)
+    torch.cuda.synchronize()
+    ref = (logits.clone(), out.clone(), al.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            m.step(hidden, dl_t, x_t, B, K, 1.0, 0, 0, logits, out, al, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        logits.fill_(float("nan"))
+        out.fill_(-7)
+        al.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, ref[0]) and torch.equal(out, ref[1]) and torch.equal(al, ref[2])
+        _ = (hidden * 2).sum().item()      # eager work between replays

@@ -60,6 +60,16 @@ def step_work(w: workload.Workload, B: int, K: int, T: float):
     return bytes_, flops
 
 
+def _draft_tokens(zq, T, seed):
+    """Draft tokens drawn from q = softmax(zq / T) (Gumbel-max), argmax at T = 0."""
+    import torch
+    if T == 0:
+        return zq.argmax(-1).to(torch.int32).contiguous()
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    u = torch.rand(zq.shape, generator=gen, device="cuda").clamp_(1e-20, 1.0)
+    return (zq / T - torch.log(-torch.log(u))).argmax(-1).to(torch.int32).contiguous()
+
+
 def _device_inputs(w, B, K, T, sigma, seed=0):
     import torch
     import speculative_decoding_verification_step_amd as sv
@@ -76,19 +86,20 @@ def _device_inputs(w, B, K, T, sigma, seed=0):
     del model
     M = B * (K + 1)
     hidden = dev(workload.make_hidden(w, M))
-    target = sv.Model(d_up, d_down, d_gain, d_head)
-    # draft logits: the draft head reads the target's own final hidden state
-    drafter = sv.Model(d_up, d_down, d_gain, d_dhead)
-    zq = drafter.forward(hidden).view(B, K + 1, w.vocab)[:, :K].contiguous()
-    if T == 0:
-        x = zq.argmax(-1).to(torch.int32)
+    if w.wdtype == "bf16":
+        # the weights are packed once, at load time, into the tiled layout
+        target = sv.Model.packed(d_up, d_down, d_gain, d_head)
+        drafter = sv.Model.packed(d_up, d_down, d_gain, d_dhead)
+        del d_up, d_down
     else:
-        gen = torch.Generator(device="cuda").manual_seed(seed)
-        u = torch.rand(zq.shape, generator=gen, device="cuda").clamp_(1e-20, 1.0)
-        x = (zq / T - torch.log(-torch.log(u))).argmax(-1).to(torch.int32)
+        target = sv.Model(d_up, d_down, d_gain, d_head)
+        drafter = sv.Model(d_up, d_down, d_gain, d_dhead)
+    # draft logits: the draft head reads the target's own final hidden state
+    zq = drafter.forward(hidden).view(B, K + 1, w.vocab)[:, :K].contiguous()
+    x = _draft_tokens(zq, T, seed)
     del drafter, d_dhead
     torch.cuda.synchronize()
-    return target, hidden, zq, x.contiguous(), host
+    return target, hidden, zq, x, host
 
 
 def _time_step(sv, target, hidden, zq, x, B, K, T, steps, warmup, use_graph, seed=0, stp=0):
@@ -197,11 +208,12 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
     target, hidden, zq, x, host = _device_inputs(w, B, K, T, sigma)
     ms, wall, per, (logits, out, al, ws, s, one) = _time_step(
         sv, target, hidden, zq, x, B, K, T, steps, warmup, use_graph)
-    al_h = al.cpu().numpy()
-    # acceptance statistics over a few fresh uniform streams (untimed)
-    als = [al_h]
-    for stp in range(1, 8):
-        target.step(hidden, zq if T > 0 else None, x, B, K, T, 0, stp, logits, out, al, ws=ws)
+    # acceptance statistics (untimed): fresh draft-token draws from q and fresh
+    # uniform streams, so the AL law is sampled, not one draw repeated
+    als = []
+    for stp in range(16):
+        xs = _draft_tokens(zq, T, 1000 + stp)
+        target.step(hidden, zq if T > 0 else None, xs, B, K, T, 0, stp, logits, out, al, ws=ws)
         als.append(al.cpu().numpy().copy())
     als = np.concatenate(als)
     bytes_, flops = step_work(w, B, K, T)
@@ -221,7 +233,7 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
         "config": {"workload": w.name, "B": B, "K": K, "M": M, "d": w.d, "ffn": w.ffn,
                    "n_layers": w.n_layers, "vocab": w.vocab, "sigma": sigma, "temperature": T,
                    "launch": "hipgraph" if use_graph else "eager", "parallelism": "none (1 GPU)"},
-        "accepted_tokens_per_s": float(al_h.sum()) / (ms / 1e3),
+        "accepted_tokens_per_s": float(als.mean()) * B / (ms / 1e3),
         "mean_accept_len": float(als.mean()),
         "accept_len_hist": np.bincount(als, minlength=K + 2)[1:].tolist(),
         "step_ms_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2], per[(9 * len(per)) // 10]],

@@ -67,22 +67,52 @@ typedef enum {
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
+/* Storage order of the weight matrices.
+ *   SV_LAYOUT_ROW_MAJOR  [out, in] row-major.
+ *   SV_LAYOUT_TILED      bf16 only: each [rows, cols] matrix as produced by
+ *                        spec_verify_pack_weights -- 16 x 32 blocks of 1 KiB,
+ *                        each stored in the lane order of the gfx950 matrix-core
+ *                        operand, rows padded with zeros to a multiple of 16.
+ *                        Block (rt, s), rt < ceil(rows/16), s < cols/32, starts
+ *                        at element (rt * cols/32 + s) * 512, and its element
+ *                        l*8 + e (lane l = r + 16 q, r < 16, q < 4, e < 8) is
+ *                        W[rt*16 + r][s*32 + 8q + e].  Streaming the weights
+ *                        then reads one contiguous KiB per wave load. */
+typedef enum { SV_LAYOUT_ROW_MAJOR = 0, SV_LAYOUT_TILED = 1 } sv_layout;
+
 /* Target model description (host struct; the weight pointers are device
  * pointers that the model only borrows: keep them alive and unchanged until
  * sv_model_destroy).  d and ffn must be positive multiples of 64, d <= 32768;
- * vocab >= 1; n_layers >= 0.  Weight pointers must be 16-byte aligned. */
+ * vocab >= 1; n_layers >= 0.  Weight pointers must be 16-byte aligned.  With
+ * SV_LAYOUT_TILED the three matrices are in the tiled layout (w_up: n_layers
+ * consecutive tiled [ffn, d] matrices; w_down: tiled [d, ffn]; w_head: tiled
+ * [vocab, d], spec_verify_packed_elems(vocab, d) elements). */
 typedef struct {
     int32_t d;            /* model width                                      */
     int32_t ffn;          /* MLP width                                        */
     int32_t n_layers;     /* number of MLP blocks                             */
     int32_t vocab;        /* V                                                */
     int32_t wdtype;       /* sv_dtype of w_up, w_down, w_head                 */
+    int32_t layout;       /* sv_layout of w_up, w_down, w_head                */
     float rms_eps;        /* RMSNorm epsilon (>= 0)                           */
     const void* w_up;     /* [n_layers, ffn, d]                               */
     const void* w_down;   /* [n_layers, d, ffn]                               */
     const float* gain;    /* [n_layers + 1, d] fp32; last row = final norm    */
     const void* w_head;   /* [vocab, d]                                       */
 } sv_model_desc;
+
+/* Elements of the tiled copy of one bf16 [rows, cols] matrix
+ * (ceil(rows/16) * 16 * cols); 0 if rows < 1 or cols is not a positive
+ * multiple of 32. */
+size_t spec_verify_packed_elems(int32_t rows, int32_t cols);
+
+/* Packs `count` consecutive row-major bf16 [rows, cols] matrices at `src` into
+ * the tiled layout at `dst` (count * spec_verify_packed_elems(rows, cols)
+ * elements, caller-owned, must not overlap src).  Device pointers, 16-byte
+ * aligned; cols a positive multiple of 32.  A one-time preparation step done
+ * when the weights are loaded, not part of the verification step. */
+int spec_verify_pack_weights(const void* src, void* dst, int32_t rows, int32_t cols,
+                             int32_t count, void* stream);
 
 typedef struct sv_model sv_model;
 

@@ -7,7 +7,7 @@ modified rejection sampling per request.  All of it runs in the HIP kernels of
 ctypes binding and the in-tree build.
 """
 from .binding import (  # noqa: F401
-    LIB_PATH, Model, SpecVerifyError, accept, accept_workspace_bytes, lib, profile_begin,
+    LIB_PATH, Model, SpecVerifyError, accept, accept_workspace_bytes, lib, pack, profile_begin,
     profile_end, workspace,
     SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP,
 )

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
 SV_F32, SV_BF16 = 0, 1
+SV_LAYOUT_ROW_MAJOR, SV_LAYOUT_TILED = 0, 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -33,7 +34,7 @@ class SpecVerifyError(RuntimeError):
 
 class ModelDesc(ctypes.Structure):
     _fields_ = [("d", _i32), ("ffn", _i32), ("n_layers", _i32), ("vocab", _i32),
-                ("wdtype", _i32), ("rms_eps", ctypes.c_float),
+                ("wdtype", _i32), ("layout", _i32), ("rms_eps", ctypes.c_float),
                 ("w_up", _vp), ("w_down", _vp), ("gain", _vp), ("w_head", _vp)]
 
 
@@ -44,6 +45,8 @@ class KernelTime(ctypes.Structure):
 
 EXPORTS = {
     "spec_verify_abi_version": (_i32, []),
+    "spec_verify_packed_elems": (_sz, [_i32, _i32]),
+    "spec_verify_pack_weights": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "sv_model_create": (ctypes.c_int, [ctypes.POINTER(ModelDesc), ctypes.POINTER(_vp)]),
     "sv_model_destroy": (None, [_vp]),
     "spec_verify_forward_workspace_bytes": (_sz, [_vp, _i32]),
@@ -114,31 +117,78 @@ def workspace(nbytes: int, device=None) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device or "cuda")
 
 
+def pack(w, stream=None):
+    """Tiled copy of bf16 row-major weights: w is [rows, cols] or a stack
+    [count, rows, cols]; returns a flat bf16 tensor of
+    count * spec_verify_packed_elems(rows, cols) elements."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() == 2:
+        count, rows, cols = 1, w.shape[0], w.shape[1]
+    elif w.dim() == 3:
+        count, rows, cols = w.shape
+    else:
+        raise ValueError("w must be 2-D or 3-D")
+    n = int(lib().spec_verify_packed_elems(rows, cols))
+    if n == 0:
+        raise ValueError(f"cannot pack a [{rows}, {cols}] matrix (cols must be a multiple of 32)")
+    out = torch.empty(max(count * n, 1), dtype=torch.bfloat16, device=w.device)
+    if count:
+        _check(lib().spec_verify_pack_weights(_ptr(w), _ptr(out), rows, cols, count, _stream(stream)))
+    return out
+
+
 class Model:
     """Borrowed view of target weights already resident on the GPU.
 
-    w_up [L, ffn, d], w_down [L, d, ffn], w_head [V, d] (bfloat16 or float32),
+    Row-major layout: w_up [L, ffn, d], w_down [L, d, ffn], w_head [V, d]
+    (bfloat16 or float32).  Tiled layout (bf16; see ``pack``): pass the packed
+    tensors with ``layout="tiled"`` and the shapes in ``dims = (L, d, ffn, V)``.
     gain [L+1, d] float32.  The tensors are kept referenced for the model's
-    lifetime."""
+    lifetime.  ``Model.packed(...)`` packs row-major bf16 weights first."""
 
-    def __init__(self, w_up, w_down, gain, w_head, rms_eps: float = 1e-5):
+    def __init__(self, w_up, w_down, gain, w_head, rms_eps: float = 1e-5, layout: str = "row",
+                 dims=None):
         dt = w_head.dtype
         if dt not in (torch.bfloat16, torch.float32):
             raise ValueError("weights must be bfloat16 or float32")
-        V, d = w_head.shape
-        L, ffn = w_up.shape[0], w_up.shape[1]
-        _need(w_up, "w_up", dt, (L, ffn, d))
-        _need(w_down, "w_down", dt, (L, d, ffn))
+        if layout == "row":
+            V, d = w_head.shape
+            L, ffn = w_up.shape[0], w_up.shape[1]
+            _need(w_up, "w_up", dt, (L, ffn, d))
+            _need(w_down, "w_down", dt, (L, d, ffn))
+            _need(w_head, "w_head", dt, (V, d))
+            lay = SV_LAYOUT_ROW_MAJOR
+        elif layout == "tiled":
+            L, d, ffn, V = dims
+            pe = lambda r, c: int(lib().spec_verify_packed_elems(r, c))
+            _need(w_up, "w_up", torch.bfloat16)
+            _need(w_down, "w_down", torch.bfloat16)
+            _need(w_head, "w_head", torch.bfloat16)
+            if L and (w_up.numel() < L * pe(ffn, d) or w_down.numel() < L * pe(d, ffn)):
+                raise ValueError("packed block weights too small")
+            if w_head.numel() < pe(V, d):
+                raise ValueError("packed head too small")
+            lay = SV_LAYOUT_TILED
+        else:
+            raise ValueError("layout must be 'row' or 'tiled'")
         _need(gain, "gain", torch.float32, (L + 1, d))
-        _need(w_head, "w_head", dt, (V, d))
         self._keep = (w_up, w_down, gain, w_head)
         self.d, self.ffn, self.n_layers, self.vocab, self.dtype = d, ffn, L, V, dt
-        desc = ModelDesc(d, ffn, L, V, SV_BF16 if dt == torch.bfloat16 else SV_F32, rms_eps,
+        self.layout = layout
+        desc = ModelDesc(d, ffn, L, V, SV_BF16 if dt == torch.bfloat16 else SV_F32, lay, rms_eps,
                          w_up.data_ptr() if L else None, w_down.data_ptr() if L else None,
                          gain.data_ptr(), w_head.data_ptr())
         h = ctypes.c_void_p()
         _check(lib().sv_model_create(ctypes.byref(desc), ctypes.byref(h)))
         self._h = h
+
+    @classmethod
+    def packed(cls, w_up, w_down, gain, w_head, rms_eps: float = 1e-5):
+        """Pack row-major bf16 weights into the tiled layout and wrap them."""
+        L, ffn, d = w_up.shape
+        V = w_head.shape[0]
+        up, down, hd = pack(w_up), pack(w_down), pack(w_head)
+        return cls(up, down, gain, hd, rms_eps, layout="tiled", dims=(L, d, ffn, V))
 
     def __del__(self):
         h = getattr(self, "_h", None)

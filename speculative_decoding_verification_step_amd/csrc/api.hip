@@ -45,9 +45,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // ---- kernel choice ---------------------------------------------------------
-// bf16 weights: MFMA with the weights streamed straight to registers for every
-// B*(K+1) measured so far; fp32 weights: the vector-ALU GEMV.  The choice can
-// be overridden for measurement with SPEC_VERIFY_MATMUL = gemv | skinny.
+// bf16 weights: matrix cores with the weights streamed straight to registers
+// (measured faster than the vector-ALU dot products already at 5 rows);
+// fp32 weights: the vector-ALU GEMV.  For measurement, SPEC_VERIFY_MATMUL =
+// gemv | skinny overrides the choice for row-major bf16 weights.
 int forced_kind() {
     static int k = [] {
         const char* e = getenv("SPEC_VERIFY_MATMUL");
@@ -62,6 +63,7 @@ int forced_kind() {
 int matmul_kind(const sv_model_desc& d, int M) {
     (void)M;
     if (d.wdtype != SV_BF16) return kGemvValu;
+    if (d.layout == SV_LAYOUT_TILED) return kMfmaSkinny;
     const int f = forced_kind();
     if (f >= 0) return f;
     return kMfmaSkinny;
@@ -100,6 +102,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
                 hipStream_t s) {
     const ForwardPlan p = plan_forward(d, M);
     const int bf16 = d.wdtype == SV_BF16;
+    const int tiled = d.layout == SV_LAYOUT_TILED;
     const size_t es = bf16 ? 2 : 4;
     float* h = reinterpret_cast<float*>(ws + p.off_h);
     void* a = ws + p.off_a;
@@ -110,11 +113,13 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
     e = launch_rmsnorm(hidden, h, d.gain, a, M, d.d, d.rms_eps, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     for (int l = 0; l < d.n_layers; ++l) {
+        // (ffn and d are multiples of 64, so the tiled matrices have the
+        // same element counts as the row-major ones)
         MatmulArgs up{};
         up.W = static_cast<const char*>(d.w_up) + (size_t)l * d.ffn * d.d * es;
         up.act = a;
         up.M = M; up.N = d.ffn; up.K = d.d;
-        up.epi = kEpiSilu; up.out = act_s; up.bf16 = bf16;
+        up.epi = kEpiSilu; up.out = act_s; up.bf16 = bf16; up.tiled = tiled;
         e = launch_matmul(up, p.kind, s);
         if (e != hipSuccess) return hip_fail(e, "up-projection launch");
 
@@ -122,7 +127,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
         dn.W = static_cast<const char*>(d.w_down) + (size_t)l * d.d * d.ffn * es;
         dn.act = act_s;
         dn.M = M; dn.N = d.d; dn.K = d.ffn;
-        dn.epi = kEpiResidual; dn.out = h; dn.bf16 = bf16;
+        dn.epi = kEpiResidual; dn.out = h; dn.bf16 = bf16; dn.tiled = tiled;
         e = launch_matmul(dn, p.kind, s);
         if (e != hipSuccess) return hip_fail(e, "down-projection launch");
 
@@ -133,7 +138,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
     hd.W = d.w_head;
     hd.act = a;
     hd.M = M; hd.N = d.vocab; hd.K = d.d;
-    hd.epi = kEpiStore; hd.out = logits; hd.bf16 = bf16;
+    hd.epi = kEpiStore; hd.out = logits; hd.bf16 = bf16; hd.tiled = tiled;
     e = launch_matmul(hd, p.kind, s);
     if (e != hipSuccess) return hip_fail(e, "LM-head launch");
     return SV_OK;
@@ -147,24 +152,26 @@ int run_accept(const float* tl, const float* dl, const int32_t* x, int B, int K,
     const size_t n_t = (size_t)B * (K + 1), n_d = (size_t)B * K;
     const size_t nc = (size_t)stats_chunks(V);
     const size_t rows = n_t + n_d;
-    float* rmax = reinterpret_cast<float*>(ws);
-    float* rsum = reinterpret_cast<float*>(ws + align_up(rows * nc * 4));
-    int* rarg = reinterpret_cast<int*>(ws + 2 * align_up(rows * nc * 4));
+    float* pv = reinterpret_cast<float*>(ws);
+    float* ps = reinterpret_cast<float*>(ws + align_up(rows * nc * 4));
+    int* pi = reinterpret_cast<int*>(ws + 2 * align_up(rows * nc * 4));
     hipError_t e = launch_row_stats(tl, dl, (int)n_t, greedy ? 0 : (int)n_d, V, inv_t, greedy,
-                                    rmax, rsum, rarg, s);
+                                    pv, ps, pi, s);
     if (e != hipSuccess) return hip_fail(e, "row-stats launch");
-    e = launch_accept(tl, dl, x, B, K, V, inv_t, greedy, seed, step, rmax, rsum, rarg, out, al,
-                      p_at, q_at, s);
+    e = launch_accept(tl, dl, x, B, K, V, inv_t, greedy, seed, step, pv, ps, pi, out, al, p_at,
+                      q_at, s);
     if (e != hipSuccess) return hip_fail(e, "accept launch");
     return SV_OK;
 }
 
 int check_accept_args(const float* tl, const float* dl, const int32_t* x, int B, int K, int V,
                       float T, const int32_t* out, const int32_t* al) {
-    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1 (got B=%d K=%d V=%d)", B, K, V);
+    if (B < 0 || K < 0 || V < 1)
+        return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1 (got B=%d K=%d V=%d)", B, K, V);
     if ((int64_t)B * (K + 1) > INT32_MAX / 2 || (int64_t)B * (K + 1) * V > ((int64_t)1 << 40))
         return fail(SV_ERR_UNSUPPORTED, "B*(K+1)*V too large");
-    if (!temp_ok(T)) return fail(SV_ERR_INVALID_ARG, "temperature must be finite and 0 or >= FLT_MIN (got %g)", (double)T);
+    if (!temp_ok(T))
+        return fail(SV_ERR_INVALID_ARG, "temperature must be finite and 0 or >= FLT_MIN (got %g)", (double)T);
     if (B == 0) return SV_OK;
     if (!tl || !out || !al) return fail(SV_ERR_INVALID_ARG, "null target_logits / out_tokens / accept_len");
     if (K > 0 && !x) return fail(SV_ERR_INVALID_ARG, "null draft_tokens with K > 0");
@@ -220,6 +227,30 @@ int32_t spec_verify_abi_version(void) { return SV_ABI_VERSION; }
 
 const char* spec_verify_last_error(void) { return g_err.c_str(); }
 
+size_t spec_verify_packed_elems(int32_t rows, int32_t cols) {
+    if (rows < 1 || cols < 32 || cols % 32) return 0;
+    return tiled_elems(rows, cols);
+}
+
+int spec_verify_pack_weights(const void* src, void* dst, int32_t rows, int32_t cols,
+                             int32_t count, void* stream) {
+    if (rows < 1 || cols < 32 || cols % 32 || count < 0 || count > 65535)
+        return fail(SV_ERR_INVALID_ARG, "need rows >= 1, cols a positive multiple of 32, 0 <= count <= 65535");
+    if (count == 0) return SV_OK;
+    if (!src || !dst) return fail(SV_ERR_INVALID_ARG, "null src or dst");
+    if (((uintptr_t)src | (uintptr_t)dst) % 16)
+        return fail(SV_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    const size_t in_bytes = (size_t)count * rows * cols * 2;
+    const size_t out_bytes = (size_t)count * tiled_elems(rows, cols) * 2;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + out_bytes && d0 < s0 + in_bytes)
+        return fail(SV_ERR_INVALID_ARG, "src and dst overlap");
+    hipError_t e = launch_pack(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
+                               rows, cols, count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+    return SV_OK;
+}
+
 int sv_model_create(const sv_model_desc* desc, sv_model** out) {
     if (!desc || !out) return fail(SV_ERR_INVALID_ARG, "null desc or out");
     *out = nullptr;
@@ -230,6 +261,10 @@ int sv_model_create(const sv_model_desc* desc, sv_model** out) {
         return fail(SV_ERR_UNSUPPORTED, "d and ffn must be multiples of 64, d <= 32768 (got %d, %d)", d.d, d.ffn);
     if (d.wdtype != SV_F32 && d.wdtype != SV_BF16)
         return fail(SV_ERR_UNSUPPORTED, "weight dtype %d not supported", d.wdtype);
+    if (d.layout != SV_LAYOUT_ROW_MAJOR && d.layout != SV_LAYOUT_TILED)
+        return fail(SV_ERR_UNSUPPORTED, "layout %d not supported", d.layout);
+    if (d.layout == SV_LAYOUT_TILED && d.wdtype != SV_BF16)
+        return fail(SV_ERR_UNSUPPORTED, "the tiled layout holds bf16 weights only");
     if (!(d.rms_eps >= 0.0f) || !isfinite(d.rms_eps))
         return fail(SV_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
     if (!d.gain || !d.w_head || (d.n_layers > 0 && (!d.w_up || !d.w_down)))
@@ -279,7 +314,8 @@ int spec_verify_forward(const sv_model* m, const float* hidden, int32_t M, float
         return fail(SV_ERR_INVALID_ARG, "hidden and logits must be 16-byte aligned");
     const size_t need = plan_forward(m->desc, M).bytes;
     if (!ws || ws_bytes < need || (uintptr_t)ws % kAlign)
-        return fail(SV_ERR_WORKSPACE, "workspace must be %zu bytes, %d-byte aligned (got %zu)", need, (int)kAlign, ws_bytes);
+        return fail(SV_ERR_WORKSPACE, "workspace must be %zu bytes, %d-byte aligned (got %zu)", need,
+                    (int)kAlign, ws_bytes);
     return run_forward(m->desc, hidden, M, logits, static_cast<char*>(ws),
                        static_cast<hipStream_t>(stream));
 }
@@ -294,7 +330,8 @@ int spec_verify_accept(const float* target_logits, const float* draft_logits,
     if (rc != SV_OK || B == 0) return rc;
     const size_t need = accept_bytes(B, K, V);
     if (!ws || ws_bytes < need || (uintptr_t)ws % kAlign)
-        return fail(SV_ERR_WORKSPACE, "workspace must be %zu bytes, %d-byte aligned (got %zu)", need, (int)kAlign, ws_bytes);
+        return fail(SV_ERR_WORKSPACE, "workspace must be %zu bytes, %d-byte aligned (got %zu)", need,
+                    (int)kAlign, ws_bytes);
     return run_accept(target_logits, draft_logits, draft_tokens, B, K, V, temperature, seed, step,
                       out_tokens, accept_len, p_at_draft, q_at_draft, static_cast<char*>(ws),
                       static_cast<hipStream_t>(stream));
@@ -319,7 +356,8 @@ int spec_verify_step(const sv_model* m, const float* hidden, const float* draft_
     const size_t fwd = plan_forward(m->desc, M).bytes;
     const size_t need = fwd + accept_bytes(B, K, m->desc.vocab);
     if (!ws || ws_bytes < need || (uintptr_t)ws % kAlign)
-        return fail(SV_ERR_WORKSPACE, "workspace must be %zu bytes, %d-byte aligned (got %zu)", need, (int)kAlign, ws_bytes);
+        return fail(SV_ERR_WORKSPACE, "workspace must be %zu bytes, %d-byte aligned (got %zu)", need,
+                    (int)kAlign, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = run_forward(m->desc, hidden, M, logits_out, static_cast<char*>(ws), s);
     if (rc != SV_OK) return rc;

@@ -23,13 +23,21 @@ struct MatmulArgs {
     int epi;
     void* out;            // act_out (kEpiSilu), h (kEpiResidual) or f32_out (kEpiStore)
     int bf16;             // 1: bf16 weights/activations, 0: fp32
+    int tiled;            // 1: W in the MFMA-tiled layout of pack.hip (bf16 only)
 };
+
+// bf16 weights: elements of the MFMA-tiled copy of a [rows, cols] matrix
+// (rows padded to a multiple of 16), and the packing launch for `count`
+// consecutive row-major matrices.
+size_t tiled_elems(int rows, int cols);
+hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int rows, int cols, int count,
+                       hipStream_t stream);
 
 // Kernel families a matmul can run on.
 enum MatmulKind : int {
     kGemvValu = 0,        // VALU dot products, M <= 8 per launch (m-chunks above)
     kMfmaSkinny = 1,      // bf16 MFMA, weights streamed straight to registers
-    kMfmaTiled = 2,       // bf16 MFMA, LDS-staged tiles for large M
+    kMfmaTiled = 2,       // bf16 MFMA, LDS-staged blocks for large M
 };
 
 hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream);

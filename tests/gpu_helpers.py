@@ -41,9 +41,10 @@ def to_dev_weight(w: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(w)).cuda()
 
 
-def device_model(sv, model: dict, head: str = "w_head"):
-    return sv.Model(to_dev_weight(model["w_up"]), to_dev_weight(model["w_down"]),
-                    torch.from_numpy(model["gain"]).cuda(), to_dev_weight(model[head]))
+def device_model(sv, model: dict, head: str = "w_head", tiled: bool = False):
+    args = (to_dev_weight(model["w_up"]), to_dev_weight(model["w_down"]),
+            torch.from_numpy(model["gain"]).cuda(), to_dev_weight(model[head]))
+    return sv.Model.packed(*args) if tiled else sv.Model(*args)
 
 
 def cpu(t: torch.Tensor) -> np.ndarray:

@@ -50,11 +50,12 @@ def test_abi_version(L):
 
 
 def _desc(**kw):
-    base = dict(d=256, ffn=1024, n_layers=2, vocab=4096, wdtype=bd.SV_BF16, rms_eps=1e-5,
-                w_up=FAKE, w_down=FAKE, gain=FAKE, w_head=FAKE)
+    base = dict(d=256, ffn=1024, n_layers=2, vocab=4096, wdtype=bd.SV_BF16, layout=0,
+                rms_eps=1e-5, w_up=FAKE, w_down=FAKE, gain=FAKE, w_head=FAKE)
     base.update(kw)
     return bd.ModelDesc(base["d"], base["ffn"], base["n_layers"], base["vocab"], base["wdtype"],
-                        base["rms_eps"], base["w_up"], base["w_down"], base["gain"], base["w_head"])
+                        base["layout"], base["rms_eps"], base["w_up"], base["w_down"],
+                        base["gain"], base["w_head"])
 
 
 def _create(L, **kw):
@@ -69,6 +70,7 @@ def _create(L, **kw):
     (dict(ffn=1000), bd.SV_ERR_UNSUPPORTED), (dict(wdtype=7), bd.SV_ERR_UNSUPPORTED),
     (dict(rms_eps=-1.0), bd.SV_ERR_INVALID_ARG), (dict(rms_eps=float("nan")), bd.SV_ERR_INVALID_ARG),
     (dict(w_head=0), bd.SV_ERR_INVALID_ARG), (dict(w_up=FAKE + 4), bd.SV_ERR_INVALID_ARG),
+    (dict(layout=2), bd.SV_ERR_UNSUPPORTED), (dict(layout=1, wdtype=bd.SV_F32), bd.SV_ERR_UNSUPPORTED),
 ])
 def test_model_create_rejects(L, kw, code):
     rc, h = _create(L, **kw)
@@ -162,3 +164,16 @@ def test_forward_and_step_reject(L):
 def test_profile_state_machine(L):
     assert L.spec_verify_profile_end(None, 0, None) == bd.SV_ERR_INVALID_ARG
     assert L.spec_verify_profile_begin(0) == bd.SV_ERR_INVALID_ARG
+
+
+def test_packed_sizes_and_pack_rejects(L):
+    assert L.spec_verify_packed_elems(4096, 256) == 4096 * 256
+    assert L.spec_verify_packed_elems(1001, 256) == 1008 * 256      # rows padded to 16
+    assert L.spec_verify_packed_elems(16, 48) == 0                  # cols not a multiple of 32
+    assert L.spec_verify_packed_elems(0, 64) == 0
+    pw = L.spec_verify_pack_weights
+    assert pw(FAKE, FAKE * 4, 16, 48, 1, None) == bd.SV_ERR_INVALID_ARG
+    assert pw(0, FAKE, 16, 64, 1, None) == bd.SV_ERR_INVALID_ARG
+    assert pw(FAKE, FAKE + 8, 16, 64, 1, None) == bd.SV_ERR_INVALID_ARG     # misaligned
+    assert pw(FAKE, FAKE + 512, 16, 64, 1, None) == bd.SV_ERR_INVALID_ARG   # overlap
+    assert pw(FAKE, FAKE, 16, 64, 0, None) == 0                             # nothing to do

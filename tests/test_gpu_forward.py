@@ -40,16 +40,33 @@ def test_tiny_fp32_forward():
 
 
 @gpu
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("M", [1, 3, 5, 8, 9, 16, 40, 64, 130, 320])
-def test_small_bf16_forward_rows(M):
+def test_small_bf16_forward_rows(M, tiled):
     sv = require_gpu()
     # several tiles in every dimension plus a ragged vocabulary
     w = workload.Workload("small-bf16", 256, 768, 2, 1001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 1)
     model = workload.make_model(w, draft_head=False)
-    m = device_model(sv, model)
+    m = device_model(sv, model, tiled=tiled)
     h = workload.make_hidden(w, M, sub=M)
     z = cpu(m.forward(torch.from_numpy(h).cuda()))
-    _check(z, of.forward(model, h), TOL_BF16, f"small bf16 M={M}")
+    _check(z, of.forward(model, h), TOL_BF16, f"small bf16 M={M} tiled={tiled}")
+
+
+@gpu
+@pytest.mark.parametrize("rows,cols,count", [(16, 32, 1), (1001, 256, 1), (48, 96, 3), (4096, 4096, 1)])
+def test_pack_matches_layout_definition(rows, cols, count):
+    """The packed copy follows the documented tile order element by element."""
+    sv = require_gpu()
+    g = np.random.default_rng(rows + cols)
+    src = g.integers(0, 1 << 16, size=(count, rows, cols), dtype=np.uint16)
+    got = cpu(sv.pack(to_dev_weight(src)).view(torch.int16)).view(np.uint16)
+    rp = (rows + 15) // 16 * 16
+    pad = np.zeros((count, rp, cols), np.uint16)
+    pad[:, :rows] = src
+    # [count, rt, r, s, q, e] -> [count, rt, s, q, r, e]
+    want = pad.reshape(count, rp // 16, 16, cols // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5)
+    assert np.array_equal(got, want.reshape(-1))
 
 
 @gpu
@@ -71,7 +88,7 @@ def _full_size(name, rows):
     hid = torch.from_numpy(hidden).cuda()
     for L in (0, 1, 2, w.n_layers):
         gain = torch.ones((L + 1, w.d), dtype=torch.float32, device="cuda")
-        m = sv.Model(d_up[:L], d_down[:L], gain, d_head)
+        m = sv.Model.packed(d_up[:L], d_down[:L], gain, d_head)    # the benchmark's layout
         z = cpu(m.forward(hid))
         ref = of.forward(of.truncated(model, L), hidden[rows])
         tol = TOL_BF16 if L < w.n_layers else full_stack_tol(name)

@@ -34,7 +34,7 @@ def _step_case(name, requests, T=None, step=0, seed=0):
     x = workload.make_random_tokens(B, K, V, seed=seed)
     x[requests] = ov.sample_draft_tokens(dl[requests], T, seed, step)
 
-    m = device_model(sv, model)
+    m = device_model(sv, model, tiled=w.wdtype == "bf16")
     logits, out, al = m.step(torch.from_numpy(hidden).cuda(), torch.from_numpy(dl).cuda(),
                              torch.from_numpy(x).cuda(), B, K, T, seed, step)
     torch.cuda.synchronize()

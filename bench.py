@@ -60,6 +60,29 @@ def step_work(w: workload.Workload, B: int, K: int, T: float):
     return bytes_, flops
 
 
+def measured_traffic(workload_name: str, kernel_label: str):
+    """HBM bytes per launch of `kernel_label` from the committed counter
+    summary (profiles/hbm_traffic_*.md: FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy of known size), or None if there is none for this workload or
+    the kernel sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    pkg = os.path.join(ROOT, "speculative_decoding_verification_step_amd")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.md"))):
+        m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("workload") != workload_name or kernel_label not in rec["hbm_bytes_per_launch"]:
+            continue
+        src = b"".join(open(os.path.join(pkg, f), "rb").read() for f in rec["kernel_sources"])
+        if hashlib.sha256(src).hexdigest() != rec["kernel_sources_sha256"]:
+            return None
+        return rec["hbm_bytes_per_launch"][kernel_label]
+    return None
+
+
 def _draft_tokens(zq, T, seed):
     """Draft tokens drawn from q = softmax(zq / T) (Gumbel-max), argmax at T = 0."""
     import torch
@@ -257,7 +280,7 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
             roof = {"bound": "mfma", "achieved": f / n / avg_s / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = None
+        roof["traffic"] = measured_traffic(w.name, dom) if (B, K) == (w.B, w.K) else None
         roof["kernel"] = dom
         roof["avg_launch_us"] = avg_s * 1e6
         roof["algorithmic_bytes_per_launch"] = b / n
@@ -287,6 +310,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="finish with one plain 256 MiB device copy (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
@@ -317,6 +342,14 @@ def main():
     res = run_point(w, B, K, sigma, T, a.steps, a.warmup, not a.eager, not a.no_cpu_baseline,
                     profile=not a.no_profile)
     print(json.dumps(res), flush=True)
+    if a.calib_copy:
+        # a plain copy of known size: 256 MiB read + 256 MiB written, so the
+        # HBM byte counters of the kernels above can be scaled by it
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)        # one elementwise kernel: read + write 256 MiB
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

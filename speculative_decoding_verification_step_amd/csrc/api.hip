@@ -93,7 +93,8 @@ ForwardPlan plan_forward(const sv_model_desc& d, int M) {
 size_t accept_bytes(int B, int K, int V) {
     const size_t nc = (size_t)stats_chunks(V);
     const size_t rows = (size_t)B * (K + 1) + (size_t)B * K;
-    return align_up(rows * nc * 4) * 2 + align_up((size_t)B * (K + 1) * nc * 4);
+    return align_up(rows * nc * 4) * 2 + align_up((size_t)B * (K + 1) * nc * 4) +
+           align_up(accept_meta_floats(B, V) * 4);
 }
 
 bool temp_ok(float T) { return isfinite(T) && (T == 0.0f || T >= FLT_MIN); }
@@ -155,11 +156,13 @@ int run_accept(const float* tl, const float* dl, const int32_t* x, int B, int K,
     float* pv = reinterpret_cast<float*>(ws);
     float* ps = reinterpret_cast<float*>(ws + align_up(rows * nc * 4));
     int* pi = reinterpret_cast<int*>(ws + 2 * align_up(rows * nc * 4));
+    float* scratch = reinterpret_cast<float*>(ws + 2 * align_up(rows * nc * 4) +
+                                              align_up(n_t * nc * 4));
     hipError_t e = launch_row_stats(tl, dl, (int)n_t, greedy ? 0 : (int)n_d, V, inv_t, greedy,
                                     pv, ps, pi, s);
     if (e != hipSuccess) return hip_fail(e, "row-stats launch");
-    e = launch_accept(tl, dl, x, B, K, V, inv_t, greedy, seed, step, pv, ps, pi, out, al, p_at,
-                      q_at, s);
+    e = launch_accept(tl, dl, x, B, K, V, inv_t, greedy, seed, step, pv, ps, pi, scratch, out, al,
+                      p_at, q_at, s);
     if (e != hipSuccess) return hip_fail(e, "accept launch");
     return SV_OK;
 }
@@ -200,21 +203,16 @@ ProfState& prof() {
 
 }  // namespace
 
-ProfScope::ProfScope(const char* name, hipStream_t s, double bytes, double flops)
-    : slot(-1), stream(s) {
+ProfScope::ProfScope(const char* name, hipStream_t s, double bytes, double flops) {
+    (void)s;
     ProfState& p = prof();
     if (!p.on) return;
     std::lock_guard<std::mutex> g(p.mu);
     if (!p.on || (int)p.recs.size() >= p.cap) return;
-    slot = (int)p.recs.size();
+    const size_t slot = p.recs.size();
     p.recs.push_back({name, bytes, flops});
-    (void)hipEventRecord(p.ev[2 * slot], s);
-}
-
-ProfScope::~ProfScope() {
-    if (slot < 0) return;
-    ProfState& p = prof();
-    (void)hipEventRecord(p.ev[2 * slot + 1], stream);
+    ev0 = p.ev[2 * slot];
+    ev1 = p.ev[2 * slot + 1];
 }
 
 }  // namespace sv

@@ -124,9 +124,11 @@ hipError_t launch_gemv_rows(const MatmulArgs& a, int mb, int mc, hipStream_t str
     const size_t out_es = (EPI == kEpiSilu) ? es : 4;
     void* out = static_cast<char*>(a.out) + (size_t)mb * a.N * out_es;
     const dim3 grid((a.N + kWaves * kRowsPerWave - 1) / (kWaves * kRowsPerWave));
+    ProfScope prof(a.name, stream, matmul_bytes(a, mc), 2.0 * mc * (double)a.N * a.K);
 #define SV_GEMV_CASE(MBV)                                                                  \
     case MBV:                                                                              \
-        gemv_kernel<kBf16, MBV, EPI><<<grid, kThreads, 0, stream>>>(a.W, A, a.N, a.K, out, a.N); \
+        SV_LAUNCH(prof, (gemv_kernel<kBf16, MBV, EPI>), grid, kThreads, stream, a.W, A, a.N, a.K, \
+                  out, a.N);                                                               \
         break;
     switch (mc) {
         SV_GEMV_CASE(1) SV_GEMV_CASE(2) SV_GEMV_CASE(3) SV_GEMV_CASE(4)

@@ -3,6 +3,7 @@
 // launch status (hipGetLastError after the launch).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -24,6 +25,7 @@ struct MatmulArgs {
     void* out;            // act_out (kEpiSilu), h (kEpiResidual) or f32_out (kEpiStore)
     int bf16;             // 1: bf16 weights/activations, 0: fp32
     int tiled;            // 1: W in the MFMA-tiled layout of pack.hip (bf16 only)
+    const char* name;     // timing label, set by launch_matmul
 };
 
 // bf16 weights: elements of the MFMA-tiled copy of a [rows, cols] matrix
@@ -41,6 +43,8 @@ enum MatmulKind : int {
 };
 
 hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream);
+// Algorithmic bytes of one launch of `a` over `rows` of its activations.
+double matmul_bytes(const MatmulArgs& a, int rows);
 
 // RMSNorm of each row:  act = round_act(h / sqrt(mean(h^2) + eps) * gain)
 // with h = src; when hout != src the row is also copied to hout (the first
@@ -57,20 +61,30 @@ hipError_t launch_row_stats(const float* target, const float* draft, int n_t, in
                             float inv_t, int greedy, float* pv, float* ps, int* pi,
                             hipStream_t stream);
 
-// Accept / resample / bonus for B requests (one workgroup each), folding the
-// chunk statistics written by launch_row_stats.
+// Accept / resample / bonus for B requests, folding the chunk statistics
+// written by launch_row_stats.  `scratch` holds accept_meta_floats(B, V)
+// floats (per-chunk draw sums and per-request draw parameters).
+size_t accept_meta_floats(int B, int V);
 hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens, int B,
                          int K, int V, float inv_t, int greedy, uint64_t seed, uint32_t step,
-                         const float* pv, const float* ps, const int* pi, int32_t* out_tokens,
-                         int32_t* accept_len, float* p_at, float* q_at, hipStream_t stream);
+                         const float* pv, const float* ps, const int* pi, float* scratch,
+                         int32_t* out_tokens, int32_t* accept_len, float* p_at, float* q_at,
+                         hipStream_t stream);
 
-// Per-launch timing hook (implemented by the host layer): brackets one
-// launch with events when profiling is on.
+// Per-launch timing hook (implemented by the host layer).  When profiling is
+// on, a scope hands out a pair of events that the launch records at the
+// dispatch's own start and end (hipExtLaunchKernelGGL), so the measured time
+// is the kernel's execution, not the gaps around it; otherwise both are null
+// and the launch is an ordinary one.  One scope per kernel launch.
 struct ProfScope {
     ProfScope(const char* name, hipStream_t s, double bytes, double flops);
-    ~ProfScope();
-    int slot;
-    hipStream_t stream;
+    hipEvent_t ev0 = nullptr;
+    hipEvent_t ev1 = nullptr;
 };
+
+// Launch `kernel` (parenthesise template-ids) under a timing scope.
+#define SV_LAUNCH(prof, kernel, grid, block, stream, ...)                                  \
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, (stream), (prof).ev0, (prof).ev1, \
+                          0, __VA_ARGS__)
 
 }  // namespace sv

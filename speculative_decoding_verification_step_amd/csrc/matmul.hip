@@ -1,5 +1,6 @@
-// Dispatch of the weight-streaming matmuls to a kernel family, with the
-// per-launch timing scope (algorithmic bytes and flops of the launch).
+// Dispatch of the weight-streaming matmuls to a kernel family.  Each launch
+// below opens a timing scope with its algorithmic bytes (weights once +
+// activations + outputs; a residual is read and written) and flops.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,18 +26,24 @@ const char* scope_name(int kind, int epi) {
 hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (kind < 0 || kind > 2 || a.epi < 0 || a.epi > 2) return hipErrorInvalidValue;
+    MatmulArgs b = a;
+    b.name = scope_name(kind, a.epi);
+    switch (kind) {
+        case kGemvValu: return launch_gemv(b, stream);
+        case kMfmaSkinny: return launch_mfma_skinny(b, stream);
+        default: return launch_mfma_tiled(b, stream);
+    }
+}
+
+}  // namespace sv
+
+namespace sv {
+
+double matmul_bytes(const MatmulArgs& a, int rows) {
     const double es = a.bf16 ? 2.0 : 4.0;
     const double out_es = a.epi == kEpiSilu ? es : 4.0;
-    // weights + activations + outputs (the residual is read and written)
-    const double bytes = (double)a.N * a.K * es + (double)a.M * a.K * es +
-                         (double)a.M * a.N * out_es * (a.epi == kEpiResidual ? 2 : 1);
-    const double flops = 2.0 * a.M * (double)a.N * a.K;
-    ProfScope prof(scope_name(kind, a.epi), stream, bytes, flops);
-    switch (kind) {
-        case kGemvValu: return launch_gemv(a, stream);
-        case kMfmaSkinny: return launch_mfma_skinny(a, stream);
-        default: return launch_mfma_tiled(a, stream);
-    }
+    return (double)a.N * a.K * es + (double)rows * a.K * es +
+           (double)rows * a.N * out_es * (a.epi == kEpiResidual ? 2 : 1);
 }
 
 }  // namespace sv

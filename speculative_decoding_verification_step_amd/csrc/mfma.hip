@@ -147,12 +147,13 @@ hipError_t launch_skinny_mf(const MatmulArgs& a, const uint16_t* act, void* out,
     constexpr int RF = 1, NWK = 8;
     const dim3 grid((a.N + 16 * RF - 1) / (16 * RF));
     const uint16_t* W = static_cast<const uint16_t*>(a.W);
+    ProfScope prof(a.name, stream, matmul_bytes(a, Mc), 2.0 * Mc * (double)a.N * a.K);
     if (a.tiled)
-        mfma_skinny_kernel<MF, RF, NWK, EPI, true><<<grid, NWK * kWave, 0, stream>>>(
-            W, act, Mc, a.N, a.K, out);
+        SV_LAUNCH(prof, (mfma_skinny_kernel<MF, RF, NWK, EPI, true>), grid, NWK * kWave, stream,
+                  W, act, Mc, a.N, a.K, out);
     else
-        mfma_skinny_kernel<MF, RF, NWK, EPI, false><<<grid, NWK * kWave, 0, stream>>>(
-            W, act, Mc, a.N, a.K, out);
+        SV_LAUNCH(prof, (mfma_skinny_kernel<MF, RF, NWK, EPI, false>), grid, NWK * kWave, stream,
+                  W, act, Mc, a.N, a.K, out);
     return hipGetLastError();
 }
 

@@ -75,18 +75,18 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
 
 template <bool kBf16>
 hipError_t launch_norm_dtype(const float* src, float* hout, const float* gain, void* act, int M,
-                             int d, float eps, hipStream_t stream) {
+                             int d, float eps, hipStream_t stream, const ProfScope& prof) {
     const int n4 = d / 4;
     if (n4 <= 256) {
-        rmsnorm_kernel<kBf16, 1, 256><<<M, 256, 0, stream>>>(src, hout, gain, act, d, eps);
+        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 1, 256>), M, 256, stream, src, hout, gain, act, d, eps);
     } else if (n4 <= 1024) {
-        rmsnorm_kernel<kBf16, 1, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 1, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
     } else if (n4 <= 2048) {
-        rmsnorm_kernel<kBf16, 2, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 2, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
     } else if (n4 <= 4096) {
-        rmsnorm_kernel<kBf16, 4, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 4, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
     } else if (n4 <= 8192) {
-        rmsnorm_kernel<kBf16, 8, 1024><<<M, 1024, 0, stream>>>(src, hout, gain, act, d, eps);
+        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 8, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
     } else {
         return hipErrorInvalidValue;
     }
@@ -100,8 +100,8 @@ hipError_t launch_rmsnorm(const float* src, float* hout, const float* gain, void
     if (M <= 0) return hipSuccess;
     const double bytes = (double)M * d * (4.0 + (hout != src ? 4.0 : 0.0) + (bf16 ? 2.0 : 4.0));
     ProfScope prof("rmsnorm", stream, bytes, 0.0);
-    return bf16 ? launch_norm_dtype<true>(src, hout, gain, act, M, d, eps, stream)
-                : launch_norm_dtype<false>(src, hout, gain, act, M, d, eps, stream);
+    return bf16 ? launch_norm_dtype<true>(src, hout, gain, act, M, d, eps, stream, prof)
+                : launch_norm_dtype<false>(src, hout, gain, act, M, d, eps, stream, prof);
 }
 
 }  // namespace sv

@@ -49,7 +49,7 @@ hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int rows, int cols, i
     const size_t chunks = tiled_elems(rows, cols) / 8;
     const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)count);
     ProfScope prof("pack_weights", stream, 2.0 * count * (double)rows * cols * 2, 0.0);
-    pack_kernel<<<grid, 256, 0, stream>>>(src, dst, rows, cols, chunks);
+    SV_LAUNCH(prof, pack_kernel, grid, 256, stream, src, dst, rows, cols, chunks);
     return hipGetLastError();
 }
 

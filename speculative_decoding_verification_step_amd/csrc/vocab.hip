@@ -15,11 +15,20 @@
 // bit-identical p and q.  A draw over weights w (ascending token ids) picks
 // the smallest y whose running sum exceeds u' * sum(w).
 //
-// Layout of the work: the statistics kernel splits every row into chunks of
-// kChunk logits (one workgroup each, all of a thread's loads in flight at
-// once) and writes per-chunk (max, sum) or (max, argmax) pairs; the accept
-// kernel (one workgroup per request) folds the chunk pairs of the rows it
-// needs in chunk order, decides, and draws.
+// Three launches, all parallel over (request, chunk of kChunk logits):
+//   row_stats     per (row, chunk): (max, sum of exp) or (max, argmax), all of
+//                 a thread's loads in flight at once;
+//   decide_chunk  per (request, chunk): folds the chunk pairs of the rows it
+//                 needs (in chunk order), takes the request's accept decisions
+//                 (every chunk block of a request reaches the same ones), and
+//                 sums the weights of the draw row over its chunk;
+//   draw          per request: prefix over the chunk sums, then rescans only
+//                 the chunk that holds u' * R.
+// Within a chunk, thread t owns the run of kRun consecutive ids starting at
+// kRun * t; the running sum C_y is prefix(chunk) + exclusive(thread) +
+// running sum within the run, and the chunk total is the last thread's
+// inclusive value, computed by the same code in both kernels, so the chunk
+// that holds the threshold always contains the drawn token.
 #include <float.h>
 #include <limits.h>
 
@@ -31,12 +40,11 @@ namespace sv {
 namespace {
 
 constexpr int kStatsThreads = 256;
-constexpr int kChunk = 4096;                      // logits per statistics workgroup
+constexpr int kChunk = 4096;                       // logits per chunk workgroup
 constexpr int kPerThread = kChunk / kStatsThreads; // 16 = 4 float4
-constexpr int kAcceptThreads = 1024;
-constexpr int kAcceptWaves = kAcceptThreads / kWave;
-constexpr int kTile = 4 * kWave;                  // 256 logits per wave tile
-constexpr int kBatch = 4;                         // tiles loaded together
+constexpr int kRun = kPerThread;                   // consecutive ids per thread in a draw
+constexpr int kDrawThreads = kStatsThreads;
+constexpr int kMeta = 8;                           // per-request words passed to the draw
 
 __device__ __forceinline__ float prob(float z, float m, float inv_t, float inv_s) {
     return expf((z - m) * inv_t) * inv_s;
@@ -169,188 +177,104 @@ __device__ __forceinline__ int row_argmax(const float* pv, const int* pi, size_t
     return i == INT_MAX ? 0 : i;
 }
 
+// Weights of a draw: the residual max(0, p - q), or p alone (zd == nullptr).
 struct DrawRows {
     const float* zt;
-    const float* zd;     // nullptr: the weights are p itself
+    const float* zd;
     float mt, it_s, md, id_s, inv_t;
 };
 
-// Four consecutive logits starting at e (e % 4 == 0), -inf past the end.
-__device__ __forceinline__ f32x4 load4(const float* z, int e, int end, bool vec4) {
-    if (vec4 && e + 3 < end) return *reinterpret_cast<const f32x4*>(z + e);
-    f32x4 q;
-    q.x = e < end ? z[e] : -INFINITY;
-    q.y = e + 1 < end ? z[e + 1] : -INFINITY;
-    q.z = e + 2 < end ? z[e + 2] : -INFINITY;
-    q.w = e + 3 < end ? z[e + 3] : -INFINITY;
-    return q;
-}
-
-__device__ __forceinline__ float weight(const DrawRows& dr, float zt, float zd) {
-    const float p = prob(zt, dr.mt, dr.inv_t, dr.it_s);
+__device__ __forceinline__ float weight(const DrawRows& dr, int y) {
+    const float p = prob(dr.zt[y], dr.mt, dr.inv_t, dr.it_s);
     if (!dr.zd) return p;
-    return fmaxf(0.f, p - prob(zd, dr.md, dr.inv_t, dr.id_s));
+    return fmaxf(0.f, p - prob(dr.zd[y], dr.md, dr.inv_t, dr.id_s));
 }
 
-// Scan of one 256-logit tile by one wave: c[i] = within-tile inclusive sum at
-// lane element i (lane exclusive prefix + own running sum).  The tile total is
-// defined as the last element's inclusive sum, so both passes agree on it.
-__device__ __forceinline__ float tile_scan(const DrawRows& dr, f32x4 zt, f32x4 zd, int lane,
-                                           float c[4]) {
-    const float w0 = weight(dr, zt.x, zd.x), w1 = weight(dr, zt.y, zd.y);
-    const float w2 = weight(dr, zt.z, zd.z), w3 = weight(dr, zt.w, zd.w);
-    c[0] = w0;
-    c[1] = c[0] + w1;
-    c[2] = c[1] + w2;
-    c[3] = c[2] + w3;
-    float incl = c[3];
+// The kRun weights of thread t's run in chunk c (zero past V), as running sums.
+__device__ __forceinline__ void run_sums(const DrawRows& dr, int c, int V, float run[kRun]) {
+    const int y0 = c * kChunk + kRun * threadIdx.x;
+    float w[kRun];
+    const bool vec = (V % 4 == 0) && ((uintptr_t)dr.zt % 16 == 0) &&
+                     (!dr.zd || (uintptr_t)dr.zd % 16 == 0) && y0 + kRun <= V;
+    if (vec) {
+        // whole run in range and 16-byte aligned: four vector loads per row
+        f32x4 zt[kRun / 4], zd[kRun / 4];
+#pragma unroll
+        for (int v = 0; v < kRun / 4; ++v) {
+            zt[v] = *reinterpret_cast<const f32x4*>(dr.zt + y0 + 4 * v);
+            if (dr.zd) zd[v] = *reinterpret_cast<const f32x4*>(dr.zd + y0 + 4 * v);
+        }
+#pragma unroll
+        for (int v = 0; v < kRun / 4; ++v) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = prob(zt[v][i], dr.mt, dr.inv_t, dr.it_s);
+                w[4 * v + i] = dr.zd ? fmaxf(0.f, p - prob(zd[v][i], dr.md, dr.inv_t, dr.id_s)) : p;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) w[i] = (y0 + i < V) ? weight(dr, y0 + i) : 0.f;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+        s += w[i];
+        run[i] = s;
+    }
+}
+
+// Exclusive prefix of v over the workgroup's threads (thread order) and the
+// total, defined as the last thread's exclusive prefix plus its own value.
+__device__ __forceinline__ float block_excl_scan(float v, float* sh, float& total) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    float incl = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        const float v = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += v;
+        const float t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
     }
     float excl = __shfl_up(incl, 1, kWave);
     if (lane == 0) excl = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = excl + c[i];
-    return __shfl(c[3], kWave - 1, kWave);
+    if (lane == kWave - 1) sh[wave] = incl;
+    __syncthreads();
+    float base = 0.f;
+    for (int w = 0; w < wave; ++w) base += sh[w];
+    const float ex = base + excl;
+    if (tid == kDrawThreads - 1) sh[kDrawThreads / kWave] = ex + v;
+    __syncthreads();
+    total = sh[kDrawThreads / kWave];
+    __syncthreads();
+    return ex;
 }
 
-// Inverse-CDF draw over [0, V) by one workgroup.  Wave w owns the segment
-// [w * seg, (w + 1) * seg) (seg a multiple of 256).  Pass 1 sums each segment
-// tile by tile (kBatch tiles' loads in flight together); one thread forms the
-// segment prefix sums and the threshold t = u * R; pass 2 rescans the first
-// segment whose end exceeds t.  Returns -1 when every weight is zero.
-__device__ int block_draw(const DrawRows& dr, int V, float u, bool vec4, float* sh_seg,
-                          int* sh_tok) {
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int seg = ((V + kAcceptWaves - 1) / kAcceptWaves + kTile - 1) / kTile * kTile;
-    const int sb = min(V, wave * seg);
-    const int se = min(V, sb + seg);
-
-    float total = 0.f;
-    for (int b0 = sb; b0 < se; b0 += kBatch * kTile) {
-        f32x4 zt[kBatch], zd[kBatch];
-#pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-            const int e = b0 + t * kTile + 4 * lane;
-            zt[t] = load4(dr.zt, e, se, vec4);
-            zd[t] = dr.zd ? load4(dr.zd, e, se, vec4) : zt[t];
-        }
-#pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-            if (b0 + t * kTile >= se) break;
-            float c[4];
-            total += tile_scan(dr, zt[t], zd[t], lane, c);
-        }
-    }
-    if (lane == 0) sh_seg[wave] = total;
-    __syncthreads();
-    if (tid == 0) {
-        float pre = 0.f;
-        for (int w = 0; w < kAcceptWaves; ++w) {
-            const float nxt = pre + sh_seg[w];
-            sh_seg[w] = pre;              // becomes the exclusive prefix
-            pre = nxt;
-        }
-        sh_seg[kAcceptWaves] = pre;       // total R
-        const float t = u * pre;
-        int target_w = -1;
-        for (int w = 0; w < kAcceptWaves; ++w) {
-            const float end = (w + 1 < kAcceptWaves) ? sh_seg[w + 1] : pre;
-            if (end > t) {
-                target_w = w;
-                break;
-            }
-        }
-        sh_tok[0] = -1;
-        sh_tok[1] = target_w;
-        sh_seg[kAcceptWaves + 1] = t;
-    }
-    __syncthreads();
-    const int target_w = sh_tok[1];
-    const float t = sh_seg[kAcceptWaves + 1];
-    const float R = sh_seg[kAcceptWaves];
-    if (target_w >= 0 && wave == target_w) {
-        const float pre = sh_seg[wave];
-        float run = 0.f;
-        bool found = false;
-        for (int b0 = sb; b0 < se && !found; b0 += kBatch * kTile) {
-            f32x4 zt[kBatch], zd[kBatch];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int e = b0 + q * kTile + 4 * lane;
-                zt[q] = load4(dr.zt, e, se, vec4);
-                zd[q] = dr.zd ? load4(dr.zd, e, se, vec4) : zt[q];
-            }
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int tb = b0 + q * kTile;
-                if (found || tb >= se) break;
-                float c[4];
-                const float tt = tile_scan(dr, zt[q], zd[q], lane, c);
-                int hit = -1;
-#pragma unroll
-                for (int i = 3; i >= 0; --i)
-                    if (tb + 4 * lane + i < se && pre + (run + c[i]) > t) hit = i;
-                const unsigned long long mask = __ballot(hit >= 0);
-                if (mask) {
-                    const int first = __ffsll((long long)mask) - 1;
-                    if (lane == first) sh_tok[0] = tb + 4 * lane + hit;
-                    found = true;
-                }
-                run += tt;
-            }
-        }
-    }
-    __syncthreads();
-    if (sh_tok[0] >= 0 || R <= 0.f) {
-        const int r = R <= 0.f ? -1 : sh_tok[0];
-        __syncthreads();
-        return r;
-    }
-    // u * R rounded up to R: take the last token with positive weight.
-    int last = -1;
-    for (int y = tid; y < V; y += kAcceptThreads) {
-        const float w = weight(dr, dr.zt[y], dr.zd ? dr.zd[y] : 0.f);
-        if (w > 0.f) last = y;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
-    if (lane == 0) sh_tok[2 + wave] = last;
-    __syncthreads();
-    int r = -1;
-    for (int w = 0; w < kAcceptWaves; ++w) r = max(r, sh_tok[2 + w]);
-    __syncthreads();
-    return r;
+// Chunk total of the draw weights (the same arithmetic as the draw's rescan).
+__device__ __forceinline__ float chunk_total(const DrawRows& dr, int c, int V, float* sh) {
+    float run[kRun];
+    run_sums(dr, c, V, run);
+    float total;
+    block_excl_scan(run[kRun - 1], sh, total);
+    return total;
 }
 
-__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft,
-    const int32_t* __restrict__ tokens, int K, int V, int nchunk, float inv_t, int greedy,
-    int vec4, uint32_t k0, uint32_t k1, uint32_t step, int n_t, const float* __restrict__ pv,
-    const float* __restrict__ ps, const int* __restrict__ pi, int32_t* __restrict__ out,
-    int32_t* __restrict__ accept_len, float* __restrict__ p_at, float* __restrict__ q_at) {
-    const int b = blockIdx.x;
+// Decisions of request b, taken by every workgroup that works on b.  Returns
+// the first rejected position (1..K) or K + 1; -1 if a draft token is out of
+// range.  Threads j0 < K also report p(x), q(x) when `report`.
+__device__ int decide(const float* target, const float* draft, const int32_t* tokens, int b, int K,
+                      int V, int nchunk, float inv_t, int greedy, uint32_t k0, uint32_t k1,
+                      uint32_t step, size_t n_t, const float* pv, const float* ps, const int* pi,
+                      bool report, float* p_at, float* q_at, int* sh_first, int* sh_bad) {
     const int tid = threadIdx.x;
-    __shared__ int sh_first;
-    __shared__ int sh_bad;
-    __shared__ float sh_seg[kAcceptWaves + 2];
-    __shared__ int sh_tok[2 + kAcceptWaves];
-    __shared__ float sh_stat[4];
     if (tid == 0) {
-        sh_first = K + 1;
-        sh_bad = 0;
+        *sh_first = K + 1;
+        *sh_bad = 0;
     }
     __syncthreads();
-
     const size_t trow0 = (size_t)b * (K + 1);
-    for (int j0 = tid; j0 < K; j0 += kAcceptThreads) {
+    for (int j0 = tid; j0 < K; j0 += kDrawThreads) {
         const int x = tokens[(size_t)b * K + j0];
         if (x < 0 || x >= V) {
-            atomicOr(&sh_bad, 1);
+            atomicOr(sh_bad, 1);
             continue;
         }
         const size_t rt = trow0 + j0;
@@ -370,66 +294,212 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
             const float u = u_accept(philox_word0((uint32_t)b, (uint32_t)(j0 + 1), 0u, step, k0, k1));
             ok = (u <= p / q);      // q == 0: +inf (accept) or NaN (p == 0: reject)
         }
-        if (p_at) p_at[(size_t)b * K + j0] = p;
-        if (q_at) q_at[(size_t)b * K + j0] = q;
-        if (!ok) atomicMin(&sh_first, j0 + 1);
+        if (report) {
+            if (p_at) p_at[(size_t)b * K + j0] = p;
+            if (q_at) q_at[(size_t)b * K + j0] = q;
+        }
+        if (!ok) atomicMin(sh_first, j0 + 1);
     }
     __syncthreads();
+    const int r = *sh_bad ? -1 : *sh_first;
+    __syncthreads();
+    return r;
+}
 
-    int32_t* ob = out + trow0;
-    if (sh_bad) {
-        for (int y = tid; y <= K; y += kAcceptThreads) ob[y] = -1;
-        if (tid == 0) accept_len[b] = 0;
+__device__ __forceinline__ void write_outputs(int32_t* out, int32_t* accept_len,
+                                              const int32_t* tokens, int b, int K, int js,
+                                              int tok) {
+    int32_t* ob = out + (size_t)b * (K + 1);
+    for (int y = threadIdx.x; y <= K; y += kDrawThreads) {
+        int32_t v = -1;
+        if (js > 0) {
+            if (y < js - 1) v = tokens[(size_t)b * K + y];
+            else if (y == js - 1) v = tok;
+        }
+        ob[y] = v;
+    }
+    if (threadIdx.x == 0) accept_len[b] = js > 0 ? js : 0;
+}
+
+__global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft,
+    const int32_t* __restrict__ tokens, int K, int V, int nchunk, float inv_t, int greedy,
+    uint32_t k0, uint32_t k1, uint32_t step, const float* __restrict__ pv,
+    const float* __restrict__ ps, const int* __restrict__ pi, float* __restrict__ ctot,
+    float* __restrict__ meta, int32_t* __restrict__ out, int32_t* __restrict__ accept_len,
+    float* __restrict__ p_at, float* __restrict__ q_at, int B) {
+    const int b = blockIdx.x / nchunk;
+    const int c = blockIdx.x - b * nchunk;
+    __shared__ int sh_first, sh_bad;
+    __shared__ float sh[kDrawThreads / kWave + 1];
+    __shared__ float sh_stat[4];
+    const size_t n_t = (size_t)B * (K + 1);
+    const int js = decide(target, draft, tokens, b, K, V, nchunk, inv_t, greedy, k0, k1, step, n_t,
+                          pv, ps, pi, c == 0, p_at, q_at, &sh_first, &sh_bad);
+    if (js < 0 || greedy) {
+        // nothing to draw: the first chunk's workgroup writes the request
+        if (c == 0) {
+            const int tok = js < 0 ? -1 : row_argmax(pv, pi, (size_t)b * (K + 1) + js - 1, nchunk);
+            write_outputs(out, accept_len, tokens, b, K, js, tok);
+            if (threadIdx.x == 0) meta[(size_t)b * kMeta] = __int_as_float(0);
+        }
         return;
     }
-    const int js = sh_first;                 // 1..K: first rejection; K+1: all accepted
-    const size_t rt = trow0 + js - 1;
-    int tok;
-    if (greedy) {
-        tok = row_argmax(pv, pi, rt, nchunk);
-    } else {
-        const bool resid = js <= K;
-        const size_t rd = (size_t)b * K + js - 1;
-        if (tid == 0) {
-            float m, s;
-            row_lse(pv, ps, rt, nchunk, inv_t, m, s);
-            sh_stat[0] = m;
-            sh_stat[1] = 1.0f / s;
-            if (resid) {
-                row_lse(pv, ps, n_t + rd, nchunk, inv_t, m, s);
-                sh_stat[2] = m;
-                sh_stat[3] = 1.0f / s;
+    const size_t rt = (size_t)b * (K + 1) + js - 1;
+    const bool resid = js <= K;
+    const size_t rd = (size_t)b * K + js - 1;
+    if (threadIdx.x == 0) {
+        float m, s;
+        row_lse(pv, ps, rt, nchunk, inv_t, m, s);
+        sh_stat[0] = m;
+        sh_stat[1] = 1.0f / s;
+        sh_stat[2] = 0.f;
+        sh_stat[3] = 0.f;
+        if (resid) {
+            row_lse(pv, ps, n_t + rd, nchunk, inv_t, m, s);
+            sh_stat[2] = m;
+            sh_stat[3] = 1.0f / s;
+        }
+    }
+    __syncthreads();
+    DrawRows dr;
+    dr.zt = target + rt * V;
+    dr.zd = resid ? draft + rd * V : nullptr;
+    dr.mt = sh_stat[0];
+    dr.it_s = sh_stat[1];
+    dr.md = sh_stat[2];
+    dr.id_s = sh_stat[3];
+    dr.inv_t = inv_t;
+    const float tot = chunk_total(dr, c, V, sh);
+    if (threadIdx.x == 0) {
+        ctot[(size_t)b * nchunk + c] = tot;
+        if (c == 0) {
+            float* mb = meta + (size_t)b * kMeta;
+            mb[0] = __int_as_float(js);
+            mb[1] = dr.mt;
+            mb[2] = dr.it_s;
+            mb[3] = dr.md;
+            mb[4] = dr.id_s;
+        }
+    }
+}
+
+// Smallest y of chunk c with prefix + C_y > t (C as in run_sums / the block
+// scan); -1 if none.
+__device__ int find_in_chunk(const DrawRows& dr, int c, int V, float prefix, float t, float* sh,
+                             int* sh_hit) {
+    float run[kRun];
+    run_sums(dr, c, V, run);
+    float total;
+    const float ex = block_excl_scan(run[kRun - 1], sh, total);
+    if (threadIdx.x == 0) *sh_hit = INT_MAX;
+    __syncthreads();
+    const int y0 = c * kChunk + kRun * threadIdx.x;
+    int hit = INT_MAX;
+#pragma unroll
+    for (int i = kRun - 1; i >= 0; --i)
+        if (y0 + i < V && prefix + (ex + run[i]) > t) hit = y0 + i;
+    if (hit != INT_MAX) atomicMin(sh_hit, hit);
+    __syncthreads();
+    const int r = *sh_hit;
+    __syncthreads();
+    return r == INT_MAX ? -1 : r;
+}
+
+__global__ __launch_bounds__(kDrawThreads) void draw_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft,
+    const int32_t* __restrict__ tokens, int K, int V, int nchunk, float inv_t, uint32_t k0,
+    uint32_t k1, uint32_t step, const float* __restrict__ ctot, const float* __restrict__ meta,
+    int32_t* __restrict__ out, int32_t* __restrict__ accept_len) {
+    const int b = blockIdx.x;
+    const float* mb = meta + (size_t)b * kMeta;
+    const int js = __float_as_int(mb[0]);
+    if (js <= 0) return;                       // written by decide_chunk_kernel
+    __shared__ float sh[kDrawThreads / kWave + 1];
+    __shared__ float sh_c[2];
+    __shared__ int sh_i[2];
+    const bool resid = js <= K;
+    DrawRows dr;
+    dr.zt = target + ((size_t)b * (K + 1) + js - 1) * V;
+    dr.zd = resid ? draft + ((size_t)b * K + js - 1) * V : nullptr;
+    dr.mt = mb[1];
+    dr.it_s = mb[2];
+    dr.md = mb[3];
+    dr.id_s = mb[4];
+    dr.inv_t = inv_t;
+    const float u = u_resample(philox_word0((uint32_t)b, (uint32_t)js, 1u, step, k0, k1));
+    const float* ct = ctot + (size_t)b * nchunk;
+
+    // R, the threshold and its chunk (thread 0, chunk order).  R == 0 after a
+    // rejection (the residual mass rounded away) falls back to p; its chunk
+    // sums are recomputed here.
+    float R = 0.f;
+    if (threadIdx.x == 0)
+        for (int c = 0; c < nchunk; ++c) R += ct[c];
+    if (threadIdx.x == 0) sh_c[0] = R;
+    __syncthreads();
+    R = sh_c[0];
+    const bool fallback = !(R > 0.f);
+    if (fallback) dr.zd = nullptr;
+
+    int tok = -1;
+    float pre = 0.f;
+    int cstar = -1;
+    if (threadIdx.x == 0) {
+        sh_i[0] = -1;
+        sh_c[1] = 0.f;
+    }
+    if (!fallback) {
+        if (threadIdx.x == 0) {
+            const float t = u * R;
+            float p = 0.f;
+            for (int c = 0; c < nchunk; ++c) {
+                const float nxt = p + ct[c];
+                if (nxt > t) {
+                    sh_i[0] = c;
+                    sh_c[1] = p;
+                    break;
+                }
+                p = nxt;
             }
         }
         __syncthreads();
-        DrawRows dr;
-        dr.zt = target + rt * V;
-        dr.mt = sh_stat[0];
-        dr.it_s = sh_stat[1];
-        dr.inv_t = inv_t;
-        dr.zd = resid ? draft + rd * V : nullptr;
-        dr.md = resid ? sh_stat[2] : 0.f;
-        dr.id_s = resid ? sh_stat[3] : 0.f;
-        const float u = u_resample(philox_word0((uint32_t)b, (uint32_t)js, 1u, step, k0, k1));
-        tok = block_draw(dr, V, u, vec4, sh_seg, sh_tok);
-        if (tok < 0 && dr.zd) {              // residual mass rounded to zero: draw from p
-            dr.zd = nullptr;
-            tok = block_draw(dr, V, u, vec4, sh_seg, sh_tok);
+        cstar = sh_i[0];
+        pre = sh_c[1];
+        if (cstar >= 0) tok = find_in_chunk(dr, cstar, V, pre, u * R, sh, &sh_i[1]);
+    } else {
+        // draw from p: chunk totals of p, then the same search
+        float p = 0.f, t = 0.f;
+        float tots = 0.f;
+        for (int c = 0; c < nchunk; ++c) tots += chunk_total(dr, c, V, sh);
+        t = u * tots;
+        for (int c = 0; c < nchunk && tok < 0; ++c) {
+            const float ctc = chunk_total(dr, c, V, sh);
+            if (p + ctc > t) tok = find_in_chunk(dr, c, V, p, t, sh, &sh_i[1]);
+            p += ctc;
         }
-        if (tok < 0) tok = 0;
     }
-    for (int y = tid; y <= K; y += kAcceptThreads) {
-        int32_t v = -1;
-        if (y < js - 1) v = tokens[(size_t)b * K + y];
-        else if (y == js - 1) v = tok;
-        ob[y] = v;
+    if (tok < 0) {
+        // u * R rounded up to R: the last token with positive weight
+        int last = -1;
+        for (int y = threadIdx.x; y < V; y += kDrawThreads)
+            if (weight(dr, y) > 0.f) last = y;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+        if (threadIdx.x == 0) sh_i[1] = -1;
+        __syncthreads();
+        if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sh_i[1], last);
+        __syncthreads();
+        tok = sh_i[1] < 0 ? 0 : sh_i[1];
     }
-    if (tid == 0) accept_len[b] = js;
+    write_outputs(out, accept_len, tokens, b, K, js, tok);
 }
 
 }  // namespace
 
 int stats_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+size_t accept_meta_floats(int B, int V) { return (size_t)B * stats_chunks(V) + (size_t)B * kMeta; }
 
 hipError_t launch_row_stats(const float* target, const float* draft, int n_t, int n_d, int V,
                             float inv_t, int greedy, float* pv, float* ps, int* pi,
@@ -440,24 +510,34 @@ hipError_t launch_row_stats(const float* target, const float* draft, int n_t, in
     const int vec4 = (V % 4 == 0) && ((uintptr_t)target % 16 == 0) &&
                      (draft == nullptr || (uintptr_t)draft % 16 == 0);
     ProfScope prof("row_stats", stream, (double)rows * V * 4.0, 0.0);
-    row_stats_kernel<<<rows * nchunk, kStatsThreads, 0, stream>>>(
-        target, draft, n_t, V, nchunk, inv_t, greedy, vec4, pv, ps, pi);
+    SV_LAUNCH(prof, row_stats_kernel, rows * nchunk, kStatsThreads, stream, target, draft, n_t, V,
+              nchunk, inv_t, greedy, vec4, pv, ps, pi);
     return hipGetLastError();
 }
 
 hipError_t launch_accept(const float* target, const float* draft, const int32_t* tokens, int B,
                          int K, int V, float inv_t, int greedy, uint64_t seed, uint32_t step,
-                         const float* pv, const float* ps, const int* pi, int32_t* out_tokens,
-                         int32_t* accept_len, float* p_at, float* q_at, hipStream_t stream) {
+                         const float* pv, const float* ps, const int* pi, float* scratch,
+                         int32_t* out_tokens, int32_t* accept_len, float* p_at, float* q_at,
+                         hipStream_t stream) {
     if (B <= 0) return hipSuccess;
-    const int vec4 = (V % 4 == 0) && ((uintptr_t)target % 16 == 0) &&
-                     (draft == nullptr || (uintptr_t)draft % 16 == 0);
-    // bytes: worst case reads two rows per request twice (draw passes)
-    ProfScope prof("accept_resample", stream, (double)B * (greedy ? 0.0 : 2.0 * V * 4.0), 0.0);
-    accept_kernel<<<B, kAcceptThreads, 0, stream>>>(
-        target, draft, tokens, K, V, stats_chunks(V), inv_t, greedy, vec4,
-        (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), step, B * (K + 1), pv, ps, pi,
-        out_tokens, accept_len, p_at, q_at);
+    const int nchunk = stats_chunks(V);
+    const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
+    float* ctot = scratch;
+    float* meta = scratch + (size_t)B * nchunk;
+    {
+        // reads the draw rows once (two rows for a residual, one for a bonus)
+        ProfScope prof("decide_chunk", stream, greedy ? 0.0 : (double)B * 2.0 * V * 4.0, 0.0);
+        SV_LAUNCH(prof, decide_chunk_kernel, B * nchunk, kDrawThreads, stream, target, draft,
+                  tokens, K, V, nchunk, inv_t, greedy, k0, k1, step, pv, ps, pi, ctot, meta,
+                  out_tokens, accept_len, p_at, q_at, B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (greedy) return hipSuccess;
+    ProfScope prof("draw", stream, (double)B * 2.0 * kChunk * 4.0, 0.0);
+    SV_LAUNCH(prof, draw_kernel, B, kDrawThreads, stream, target, draft, tokens, K, V, nchunk,
+              inv_t, k0, k1, step, ctot, meta, out_tokens, accept_len);
     return hipGetLastError();
 }
 

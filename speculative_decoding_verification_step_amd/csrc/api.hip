@@ -60,10 +60,18 @@ int forced_kind() {
     return k;
 }
 
+// Above this many rows the weights are reused from LDS (kMfmaTiled); up to it
+// every weight is streamed once per pass of 64 rows (kMfmaSkinny).
+constexpr int kTiledMinRows = 65;
+
 int matmul_kind(const sv_model_desc& d, int M) {
-    (void)M;
     if (d.wdtype != SV_BF16) return kGemvValu;
-    if (d.layout == SV_LAYOUT_TILED) return kMfmaSkinny;
+    if (d.layout == SV_LAYOUT_TILED) {
+        const char* e = getenv("SPEC_VERIFY_MATMUL");
+        if (e && !strcmp(e, "skinny")) return kMfmaSkinny;
+        if (e && !strcmp(e, "tiled")) return kMfmaTiled;
+        return M >= kTiledMinRows ? kMfmaTiled : kMfmaSkinny;
+    }
     const int f = forced_kind();
     if (f >= 0) return f;
     return kMfmaSkinny;
@@ -72,18 +80,21 @@ int matmul_kind(const sv_model_desc& d, int M) {
 struct ForwardPlan {
     int M = 0;
     int kind = kGemvValu;
-    size_t off_h = 0, off_a = 0, off_s = 0, bytes = 0;
+    int splits = 0;          // kMfmaTiled: K splits of the down projection
+    size_t off_h = 0, off_a = 0, off_s = 0, off_part = 0, bytes = 0;
 };
 
 ForwardPlan plan_forward(const sv_model_desc& d, int M) {
     ForwardPlan p;
     p.M = M;
     p.kind = matmul_kind(d, M);
+    p.splits = p.kind == kMfmaTiled ? tiled_splits(M, d.d, d.ffn) : 0;
     const int es = d.wdtype == SV_BF16 ? 2 : 4;
     size_t off = 0;
     p.off_h = off; off = align_up(off + (size_t)M * d.d * 4);
     p.off_a = off; off = align_up(off + (size_t)M * d.d * es);
     p.off_s = off; off = align_up(off + (size_t)M * d.ffn * es);
+    p.off_part = off; off = align_up(off + (size_t)p.splits * M * d.d * 4);
     p.bytes = off;
     return p;
 }
@@ -108,10 +119,11 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
     float* h = reinterpret_cast<float*>(ws + p.off_h);
     void* a = ws + p.off_a;
     void* act_s = ws + p.off_s;
+    float* part = reinterpret_cast<float*>(ws + p.off_part);
     hipError_t e;
 
     // h <- hidden (the residual stream), a <- norm(h)
-    e = launch_rmsnorm(hidden, h, d.gain, a, M, d.d, d.rms_eps, bf16, s);
+    e = launch_rmsnorm(hidden, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     for (int l = 0; l < d.n_layers; ++l) {
         // (ffn and d are multiples of 64, so the tiled matrices have the
@@ -128,11 +140,16 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
         dn.W = static_cast<const char*>(d.w_down) + (size_t)l * d.d * d.ffn * es;
         dn.act = act_s;
         dn.M = M; dn.N = d.d; dn.K = d.ffn;
-        dn.epi = kEpiResidual; dn.out = h; dn.bf16 = bf16; dn.tiled = tiled;
+        dn.epi = kEpiResidual; dn.bf16 = bf16; dn.tiled = tiled;
+        // the LDS-staged GEMM leaves split-K partial planes that the next norm
+        // folds in; the streaming kernels add into h directly
+        dn.out = p.splits ? static_cast<void*>(part) : static_cast<void*>(h);
+        dn.splits = p.splits;
         e = launch_matmul(dn, p.kind, s);
         if (e != hipSuccess) return hip_fail(e, "down-projection launch");
 
-        e = launch_rmsnorm(h, h, d.gain + (size_t)(l + 1) * d.d, a, M, d.d, d.rms_eps, bf16, s);
+        e = launch_rmsnorm(h, h, part, p.splits, d.gain + (size_t)(l + 1) * d.d, a, M, d.d,
+                           d.rms_eps, bf16, s);
         if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     }
     MatmulArgs hd{};

@@ -1,0 +1,205 @@
+// LDS-staged bf16 MFMA GEMM for the verification forward at large B*(K+1).
+//
+// Once B*(K+1) reaches the hundreds the product becomes a real contraction
+// (p1 "Draft length and performance of linear layers": GEMM-M grows to
+// M(1+D) and crosses from memory- to compute-bound), and the weights must be
+// reused across many activation rows from on-chip memory instead of being
+// streamed once per 64 rows.
+//
+// out^T tile [BN weight rows x BM activation rows] per workgroup.  Each k step
+// of 32, the workgroup's waves copy BN/16 weight blocks (1 KiB each, already in
+// matrix-core operand order in the tiled layout) and BM/16 activation blocks
+// (gathered per lane from the row-major activations into the same order)
+// straight from global memory into LDS with global_load_lds_dwordx4, through
+// a ring of NS stages (NS - 1 steps in flight).  Wave (wn, wm) then reads its
+// FN weight and FM activation operands from LDS (contiguous 1 KiB each, no
+// bank conflicts) and issues FN x FM v_mfma_f32_16x16x32_bf16.  The K range can
+// be split over gridDim.z; split results go to fp32 partial planes that the
+// following RMSNorm folds in (in split order, so results are deterministic).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sv {
+
+namespace {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int WN, int WM, int FN, int FM, int NS, int EPI>
+__global__ __launch_bounds__(WN * WM * kWave) void mfma_tiled_kernel(
+    const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ act, int M, int N, int K,
+    int steps_per_split, void* __restrict__ out, size_t split_stride) {
+    constexpr int NW = WN * WM;
+    constexpr int BNF = WN * FN;                 // weight blocks (16 rows) per tile
+    constexpr int BMF = WM * FM;                 // activation blocks (16 rows) per tile
+    constexpr int FR = BNF + BMF;                // 1 KiB fragments per stage
+    static_assert(FR % NW == 0, "every wave issues the same number of copies");
+    constexpr int PER_WAVE = FR / NW;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS][FR * 512];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int wn = wave / WM, wm = wave % WM;
+    const int nb0 = blockIdx.x * BNF;            // first 16-row weight block
+    const int mb0 = blockIdx.y * BMF;
+    const int S = K / 32;
+    const int s_begin = blockIdx.z * steps_per_split;
+    const int s_end = min(S, s_begin + steps_per_split);
+    const int nblk = (N + 15) / 16;              // weight blocks present in the tiled layout
+
+    // global source of this lane's 16 bytes for fragment f at step s
+    const uint16_t* src[PER_WAVE];
+    int src_step[PER_WAVE];                      // element advance per k step
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int f = wave + NW * i;
+        if (f < BNF) {
+            const int rb = min(nb0 + f, nblk - 1);
+            src[i] = Wt + (size_t)rb * S * 512 + lane * 8;
+            src_step[i] = 512;
+        } else {
+            const int m = min((mb0 + f - BNF) * 16 + (lane & 15), M - 1);
+            src[i] = act + (size_t)m * K + 8 * (lane >> 4);
+            src_step[i] = 32;
+        }
+    }
+    auto issue = [&](int s) {
+        const int st = (s - s_begin) % NS;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int f = wave + NW * i;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(src[i] + (size_t)src_step[i] * s),
+                (lds_void*)(&lds[st][f * 512]), 16, 0, 0);
+        }
+    };
+
+    f32x4v acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (s_begin + p < s_end) issue(s_begin + p);
+
+    for (int s = s_begin; s < s_end; ++s) {
+        // the copies of step s are done once at most NS-2 later steps remain
+        if (s + NS - 2 < s_end) wait_vmcnt<PER_WAVE * (NS - 2)>();
+        else wait_vmcnt<0>();
+        // A bare workgroup barrier: this wave's copies of step s are complete
+        // (the wait above), every wave passes only after its own copies are,
+        // and every wave has finished reading step s-1's stage.  (A fenced
+        // barrier would also wait for the copies of later steps.)
+        __builtin_amdgcn_s_barrier();
+        if (s + NS - 1 < s_end) issue(s + NS - 1);
+        const uint16_t* stage = lds[(s - s_begin) % NS];
+        bf16x8 a[FN], b[FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            a[i] = *reinterpret_cast<const bf16x8*>(stage + (wn * FN + i) * 512 + lane * 8);
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            b[j] = *reinterpret_cast<const bf16x8*>(stage + (BNF + wm * FM + j) * 512 + lane * 8);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+
+    // epilogue: lane holds rows n = base + 4*(lane/16) + r, column m = lane % 16
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+        const int n = (nb0 + wn * FN + i) * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = (mb0 + wm * FM + j) * 16 + (lane & 15);
+            if (m >= M) continue;
+            const size_t o0 = (size_t)m * N + n;
+            if (n + 3 < N && (N & 3) == 0) {
+                // four consecutive outputs of one row: one vector store
+                const f32x4v v = acc[i][j];
+                if constexpr (EPI == kEpiSilu) {
+                    uint2 pk;
+                    pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
+                    pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o0) = pk;
+                } else if constexpr (EPI == kEpiResidual) {
+                    *reinterpret_cast<f32x4v*>(static_cast<float*>(out) + blockIdx.z * split_stride + o0) = v;
+                } else {
+                    *reinterpret_cast<f32x4v*>(static_cast<float*>(out) + o0) = v;
+                }
+                continue;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (n + r >= N) break;
+                const float v = acc[i][j][r];
+                const size_t o = (size_t)m * N + n + r;
+                if constexpr (EPI == kEpiSilu) {
+                    static_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(silu(v));
+                } else if constexpr (EPI == kEpiResidual) {
+                    static_cast<float*>(out)[blockIdx.z * split_stride + o] = v;   // partial plane
+                } else {
+                    static_cast<float*>(out)[o] = v;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// Tile shape: 2 x 2 waves, each 128 weight rows x 64 activation rows, so one
+// workgroup covers 256 weight rows x 128 activation rows; 4 stages of 24 KiB.
+constexpr int kTWN = 2, kTWM = 2, kTFN = 8, kTFM = 4, kTNS = 4;
+constexpr int kTileN = kTWN * kTFN * 16, kTileM = kTWM * kTFM * 16;
+
+int tiled_splits(int M, int N, int K) {
+    // enough workgroups for 256 CUs: split K when the tile grid is small
+    const long long tiles = (long long)((N + kTileN - 1) / kTileN) * ((M + kTileM - 1) / kTileM);
+    int splits = 1;
+    while (tiles * splits < 256 && splits < 8 && (K / 32) / (splits * 2) >= 16) splits *= 2;
+    return splits;
+}
+
+hipError_t launch_mfma_tiled(const MatmulArgs& a, hipStream_t stream) {
+    if (!a.bf16 || !a.tiled || a.K % 32) return hipErrorInvalidValue;
+    const int S = a.K / 32;
+    const int splits = a.epi == kEpiResidual ? a.splits : 1;
+    const int sps = (S + splits - 1) / splits;
+    const dim3 grid((a.N + kTileN - 1) / kTileN, (a.M + kTileM - 1) / kTileM, splits);
+    const dim3 block(kTWN * kTWM * kWave);
+    const size_t stride = (size_t)a.M * a.N;
+    ProfScope prof(a.name, stream, matmul_bytes(a, a.M), 2.0 * a.M * (double)a.N * a.K);
+    const uint16_t* W = static_cast<const uint16_t*>(a.W);
+    const uint16_t* X = static_cast<const uint16_t*>(a.act);
+    switch (a.epi) {
+        case kEpiSilu:
+            SV_LAUNCH(prof, (mfma_tiled_kernel<kTWN, kTWM, kTFN, kTFM, kTNS, kEpiSilu>), grid, block,
+                      stream, W, X, a.M, a.N, a.K, sps, a.out, stride);
+            break;
+        case kEpiResidual:
+            SV_LAUNCH(prof, (mfma_tiled_kernel<kTWN, kTWM, kTFN, kTFM, kTNS, kEpiResidual>), grid,
+                      block, stream, W, X, a.M, a.N, a.K, sps, a.out, stride);
+            break;
+        default:
+            SV_LAUNCH(prof, (mfma_tiled_kernel<kTWN, kTWM, kTFN, kTFM, kTNS, kEpiStore>), grid, block,
+                      stream, W, X, a.M, a.N, a.K, sps, a.out, stride);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -25,6 +25,8 @@ struct MatmulArgs {
     void* out;            // act_out (kEpiSilu), h (kEpiResidual) or f32_out (kEpiStore)
     int bf16;             // 1: bf16 weights/activations, 0: fp32
     int tiled;            // 1: W in the MFMA-tiled layout of pack.hip (bf16 only)
+    int splits;           // kMfmaTiled + kEpiResidual: K split count; `out` then
+                          // holds `splits` fp32 partial planes [M, N] (no add)
     const char* name;     // timing label, set by launch_matmul
 };
 
@@ -47,10 +49,17 @@ hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream);
 double matmul_bytes(const MatmulArgs& a, int rows);
 
 // RMSNorm of each row:  act = round_act(h / sqrt(mean(h^2) + eps) * gain)
-// with h = src; when hout != src the row is also copied to hout (the first
-// block copies the caller's hidden states into the residual stream).
-hipError_t launch_rmsnorm(const float* src, float* hout, const float* gain, void* act, int M,
-                          int d, float eps, int bf16, hipStream_t stream);
+// with h = src + part[0] + ... + part[splits-1] (split-K planes of [M, d],
+// none when splits == 0); h is written to hout when hout != src or partials
+// were folded (the first block copies the caller's hidden states into the
+// residual stream).
+hipError_t launch_rmsnorm(const float* src, float* hout, const float* part, int splits,
+                          const float* gain, void* act, int M, int d, float eps, int bf16,
+                          hipStream_t stream);
+
+// Split count of the LDS-staged GEMM's K range for an [M, N, K] product
+// (so that the tile grid fills the chip).
+int tiled_splits(int M, int N, int K);
 
 // Softmax statistics at temperature T (1/T = inv_t), per chunk of
 // stats_chunks(V) chunks of each row: chunk max and sum of exp((z - max) / T)

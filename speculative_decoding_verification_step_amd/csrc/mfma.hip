@@ -188,8 +188,4 @@ hipError_t launch_mfma_skinny(const MatmulArgs& a, hipStream_t stream) {
     }
 }
 
-hipError_t launch_mfma_tiled(const MatmulArgs& a, hipStream_t stream) {
-    return launch_mfma_skinny(a, stream);
-}
-
 }  // namespace sv

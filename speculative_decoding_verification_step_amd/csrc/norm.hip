@@ -4,7 +4,9 @@
 // a = round_act(h / sqrt(mean(h^2) + eps) * g).  One workgroup owns one row;
 // every thread holds its VPT float4 vectors of the row in registers, so all of
 // the row's loads are in flight at once, and the sum of squares is reduced
-// inside the workgroup in a fixed order.
+// inside the workgroup in a fixed order.  When the previous down projection
+// left split-K partial planes, they are folded in first, in split order:
+// h = src + (part[0] + part[1] + ...), and h is written back.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -14,7 +16,8 @@ namespace {
 
 template <bool kBf16, int VPT, int THREADS>
 __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
-    const float* src, float* hout,  // src may equal hout (then nothing is copied)
+    const float* src, float* hout,  // src may equal hout
+    const float* __restrict__ part, int splits, size_t split_stride,
     const float* __restrict__ gain, void* __restrict__ act, int d, float eps) {
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
@@ -23,12 +26,23 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src + off);
 
     f32x4 h[VPT];
-    float ss = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = tid + v * THREADS;
         h[v] = c < n4 ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (splits > 0) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = tid + v * THREADS;
+            if (c >= n4) continue;
+            f32x4 acc = reinterpret_cast<const f32x4*>(part + off)[c];
+            for (int s = 1; s < splits; ++s)
+                acc += reinterpret_cast<const f32x4*>(part + s * split_stride + off)[c];
+            h[v] += acc;
+        }
+    }
+    float ss = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         ss += h[v].x * h[v].x;
@@ -36,7 +50,7 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
         ss += h[v].z * h[v].z;
         ss += h[v].w * h[v].w;
     }
-    if (hout != src) {
+    if (hout != src || splits > 0) {
         f32x4* h4 = reinterpret_cast<f32x4*>(hout + off);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
@@ -74,34 +88,38 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
 }
 
 template <bool kBf16>
-hipError_t launch_norm_dtype(const float* src, float* hout, const float* gain, void* act, int M,
-                             int d, float eps, hipStream_t stream, const ProfScope& prof) {
+hipError_t launch_norm_dtype(const float* src, float* hout, const float* part, int splits,
+                             size_t stride, const float* gain, void* act, int M, int d, float eps,
+                             hipStream_t stream, const ProfScope& prof) {
     const int n4 = d / 4;
-    if (n4 <= 256) {
-        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 1, 256>), M, 256, stream, src, hout, gain, act, d, eps);
-    } else if (n4 <= 1024) {
-        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 1, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
-    } else if (n4 <= 2048) {
-        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 2, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
-    } else if (n4 <= 4096) {
-        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 4, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
-    } else if (n4 <= 8192) {
-        SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, 8, 1024>), M, 1024, stream, src, hout, gain, act, d, eps);
-    } else {
-        return hipErrorInvalidValue;
-    }
+#define SV_NORM(VPT, T)                                                                       \
+    SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, VPT, T>), M, T, stream, src, hout, part, splits, stride, \
+              gain, act, d, eps)
+    if (n4 <= 256) SV_NORM(1, 256);
+    else if (n4 <= 1024) SV_NORM(1, 1024);
+    else if (n4 <= 2048) SV_NORM(2, 1024);
+    else if (n4 <= 4096) SV_NORM(4, 1024);
+    else if (n4 <= 8192) SV_NORM(8, 1024);
+    else return hipErrorInvalidValue;
+#undef SV_NORM
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rmsnorm(const float* src, float* hout, const float* gain, void* act, int M,
-                          int d, float eps, int bf16, hipStream_t stream) {
+hipError_t launch_rmsnorm(const float* src, float* hout, const float* part, int splits,
+                          const float* gain, void* act, int M, int d, float eps, int bf16,
+                          hipStream_t stream) {
     if (M <= 0) return hipSuccess;
-    const double bytes = (double)M * d * (4.0 + (hout != src ? 4.0 : 0.0) + (bf16 ? 2.0 : 4.0));
+    const bool writes_h = hout != src || splits > 0;
+    const double bytes =
+        (double)M * d * (4.0 + 4.0 * splits + (writes_h ? 4.0 : 0.0) + (bf16 ? 2.0 : 4.0));
     ProfScope prof("rmsnorm", stream, bytes, 0.0);
-    return bf16 ? launch_norm_dtype<true>(src, hout, gain, act, M, d, eps, stream, prof)
-                : launch_norm_dtype<false>(src, hout, gain, act, M, d, eps, stream, prof);
+    const size_t stride = (size_t)M * d;
+    return bf16 ? launch_norm_dtype<true>(src, hout, part, splits, stride, gain, act, M, d, eps,
+                                          stream, prof)
+                : launch_norm_dtype<false>(src, hout, part, splits, stride, gain, act, M, d, eps,
+                                           stream, prof);
 }
 
 }  // namespace sv

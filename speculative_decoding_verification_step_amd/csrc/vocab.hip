@@ -40,14 +40,21 @@ namespace sv {
 namespace {
 
 constexpr int kStatsThreads = 256;
-constexpr int kChunk = 4096;                       // logits per chunk workgroup
-constexpr int kPerThread = kChunk / kStatsThreads; // 16 = 4 float4
+constexpr int kChunk = 8192;                       // logits per chunk workgroup
+constexpr int kPerThread = kChunk / kStatsThreads; // 32 = 8 float4
 constexpr int kRun = kPerThread;                   // consecutive ids per thread in a draw
 constexpr int kDrawThreads = kStatsThreads;
 constexpr int kMeta = 8;                           // per-request words passed to the draw
 
+// exp(x) on the transcendental unit: v_exp_f32(x * log2(e)).  Relative error
+// about 2^-24 * |x * log2(e)| + 1 ulp, far inside the 1e-5 decision band for
+// the exponents a softmax sees; the same function serves target and draft rows.
+__device__ __forceinline__ float fast_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 __device__ __forceinline__ float prob(float z, float m, float inv_t, float inv_s) {
-    return expf((z - m) * inv_t) * inv_s;
+    return fast_exp((z - m) * inv_t) * inv_s;
 }
 
 // (max, sum of exp((z - max) / T)) pairs, combined in a fixed order.
@@ -59,17 +66,17 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
         return;
     }
     const float mx = fmaxf(m, m2);
-    s = s * expf((m - mx) * inv_t) + s2 * expf((m2 - mx) * inv_t);
+    s = s * fast_exp((m - mx) * inv_t) + s2 * fast_exp((m2 - mx) * inv_t);
     m = mx;
 }
 
 __device__ __forceinline__ void lse_add(float& m, float& s, float v, float inv_t) {
     if (v == -INFINITY) return;
     if (v > m) {
-        s = (m == -INFINITY) ? 0.f : s * expf((m - v) * inv_t);
+        s = (m == -INFINITY) ? 0.f : s * fast_exp((m - v) * inv_t);
         m = v;
     }
-    s += expf((v - m) * inv_t);
+    s += fast_exp((v - m) * inv_t);
 }
 
 // Better (value, index): larger value, then smaller index.
@@ -162,18 +169,34 @@ __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
     }
 }
 
-// Row statistics folded from the per-chunk pairs, in chunk order.
-__device__ __forceinline__ void row_lse(const float* pv, const float* ps, size_t row, int nchunk,
-                                        float inv_t, float& m, float& s) {
+// Row statistics folded from the per-chunk pairs by one whole wave: lane l
+// folds chunks l, l+64, ... in order (all loads in flight together), then the
+// lanes are combined by a butterfly.  Both combinations are symmetric, so every
+// lane ends with the same bits, and every caller of a row gets the same ones.
+__device__ __forceinline__ void wave_row_lse(const float* pv, const float* ps, size_t row,
+                                             int nchunk, float inv_t, float& m, float& s) {
+    const int lane = threadIdx.x & (kWave - 1);
     m = -INFINITY;
     s = 0.f;
-    for (int c = 0; c < nchunk; ++c) lse_merge(m, s, pv[row * nchunk + c], ps[row * nchunk + c], inv_t);
+    for (int c = lane; c < nchunk; c += kWave)
+        lse_merge(m, s, pv[row * nchunk + c], ps[row * nchunk + c], inv_t);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float m2 = __shfl_xor(m, o, kWave);
+        const float s2 = __shfl_xor(s, o, kWave);
+        lse_merge(m, s, m2, s2, inv_t);
+    }
 }
 
-__device__ __forceinline__ int row_argmax(const float* pv, const int* pi, size_t row, int nchunk) {
+__device__ __forceinline__ int wave_row_argmax(const float* pv, const int* pi, size_t row,
+                                               int nchunk) {
+    const int lane = threadIdx.x & (kWave - 1);
     float v = -INFINITY;
     int i = INT_MAX;
-    for (int c = 0; c < nchunk; ++c) arg_merge(v, i, pv[row * nchunk + c], pi[row * nchunk + c]);
+    for (int c = lane; c < nchunk; c += kWave) arg_merge(v, i, pv[row * nchunk + c], pi[row * nchunk + c]);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1)
+        arg_merge(v, i, __shfl_xor(v, o, kWave), __shfl_xor(i, o, kWave));
     return i == INT_MAX ? 0 : i;
 }
 
@@ -259,7 +282,7 @@ __device__ __forceinline__ float chunk_total(const DrawRows& dr, int c, int V, f
 
 // Decisions of request b, taken by every workgroup that works on b.  Returns
 // the first rejected position (1..K) or K + 1; -1 if a draft token is out of
-// range.  Threads j0 < K also report p(x), q(x) when `report`.
+// range.  The wave of position j0 also reports p(x), q(x) when `report`.
 __device__ int decide(const float* target, const float* draft, const int32_t* tokens, int b, int K,
                       int V, int nchunk, float inv_t, int greedy, uint32_t k0, uint32_t k1,
                       uint32_t step, size_t n_t, const float* pv, const float* ps, const int* pi,
@@ -271,34 +294,38 @@ __device__ int decide(const float* target, const float* draft, const int32_t* to
     }
     __syncthreads();
     const size_t trow0 = (size_t)b * (K + 1);
-    for (int j0 = tid; j0 < K; j0 += kDrawThreads) {
+    const int lane = tid & (kWave - 1);
+    // one wave per draft position (the whole wave folds the row statistics)
+    for (int j0 = tid / kWave; j0 < K; j0 += kDrawThreads / kWave) {
         const int x = tokens[(size_t)b * K + j0];
         if (x < 0 || x >= V) {
-            atomicOr(sh_bad, 1);
+            if (lane == 0) atomicOr(sh_bad, 1);
             continue;
         }
         const size_t rt = trow0 + j0;
         bool ok;
         float p, q;
         if (greedy) {
-            ok = (x == row_argmax(pv, pi, rt, nchunk));
+            ok = (x == wave_row_argmax(pv, pi, rt, nchunk));
             p = ok ? 1.f : 0.f;
             q = 1.f;
         } else {
             const size_t rd = (size_t)b * K + j0;
             float mt, st, md, sd;
-            row_lse(pv, ps, rt, nchunk, inv_t, mt, st);
-            row_lse(pv, ps, n_t + rd, nchunk, inv_t, md, sd);
+            wave_row_lse(pv, ps, rt, nchunk, inv_t, mt, st);
+            wave_row_lse(pv, ps, n_t + rd, nchunk, inv_t, md, sd);
             p = prob(target[rt * V + x], mt, inv_t, 1.0f / st);
             q = prob(draft[rd * V + x], md, inv_t, 1.0f / sd);
             const float u = u_accept(philox_word0((uint32_t)b, (uint32_t)(j0 + 1), 0u, step, k0, k1));
             ok = (u <= p / q);      // q == 0: +inf (accept) or NaN (p == 0: reject)
         }
-        if (report) {
-            if (p_at) p_at[(size_t)b * K + j0] = p;
-            if (q_at) q_at[(size_t)b * K + j0] = q;
+        if (lane == 0) {
+            if (report) {
+                if (p_at) p_at[(size_t)b * K + j0] = p;
+                if (q_at) q_at[(size_t)b * K + j0] = q;
+            }
+            if (!ok) atomicMin(sh_first, j0 + 1);
         }
-        if (!ok) atomicMin(sh_first, j0 + 1);
     }
     __syncthreads();
     const int r = *sh_bad ? -1 : *sh_first;
@@ -339,7 +366,7 @@ __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
     if (js < 0 || greedy) {
         // nothing to draw: the first chunk's workgroup writes the request
         if (c == 0) {
-            const int tok = js < 0 ? -1 : row_argmax(pv, pi, (size_t)b * (K + 1) + js - 1, nchunk);
+            const int tok = js < 0 ? -1 : wave_row_argmax(pv, pi, (size_t)b * (K + 1) + js - 1, nchunk);
             write_outputs(out, accept_len, tokens, b, K, js, tok);
             if (threadIdx.x == 0) meta[(size_t)b * kMeta] = __int_as_float(0);
         }
@@ -348,17 +375,16 @@ __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
     const size_t rt = (size_t)b * (K + 1) + js - 1;
     const bool resid = js <= K;
     const size_t rd = (size_t)b * K + js - 1;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < kWave) {
         float m, s;
-        row_lse(pv, ps, rt, nchunk, inv_t, m, s);
-        sh_stat[0] = m;
-        sh_stat[1] = 1.0f / s;
-        sh_stat[2] = 0.f;
-        sh_stat[3] = 0.f;
-        if (resid) {
-            row_lse(pv, ps, n_t + rd, nchunk, inv_t, m, s);
-            sh_stat[2] = m;
-            sh_stat[3] = 1.0f / s;
+        wave_row_lse(pv, ps, rt, nchunk, inv_t, m, s);
+        float m2 = 0.f, s2 = 1.f;
+        if (resid) wave_row_lse(pv, ps, n_t + rd, nchunk, inv_t, m2, s2);
+        if (threadIdx.x == 0) {
+            sh_stat[0] = m;
+            sh_stat[1] = 1.0f / s;
+            sh_stat[2] = resid ? m2 : 0.f;
+            sh_stat[3] = resid ? 1.0f / s2 : 0.f;
         }
     }
     __syncthreads();

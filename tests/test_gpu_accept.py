@@ -50,13 +50,14 @@ def test_accept_matches_oracle(B, K, V, T, scale, sigma):
         near = compare_accept(go, ga, ro, ra, res)
         assert np.all((ga >= 1) & (ga <= K + 1))
         if T > 0 and K > 0:
-            # p(x), q(x) against the oracle's fp64 softmax (fp32 rounding only)
+            # p(x), q(x) against the oracle's fp64 softmax: fp32 sums and the exp unit
+            # (relative error ~ 2^-24 * |exponent * log2 e| + 1 ulp) stay within 5e-6
             for b in range(min(B, 8)):
                 for j in range(K):
                     p = ov.softmax(t[b, j], T)[x[b, j]]
                     q = ov.softmax(d[b, j], T)[x[b, j]]
-                    assert abs(p_at[b, j] - p) <= 2e-6 * p + 1e-30
-                    assert abs(q_at[b, j] - q) <= 2e-6 * q + 1e-30
+                    assert abs(p_at[b, j] - p) <= 5e-6 * p + 1e-30
+                    assert abs(q_at[b, j] - q) <= 5e-6 * q + 1e-30
         note(f"  seed={seed} step={step}: {B - near}/{B} requests compared, {near} near-threshold")
 
 

@@ -80,7 +80,7 @@ int matmul_kind(const sv_model_desc& d, int M) {
 struct ForwardPlan {
     int M = 0;
     int kind = kGemvValu;
-    int splits = 0;          // kMfmaTiled: K splits of the down projection
+    int splits = 0;          // K splits (partial planes) of the down projection
     size_t off_h = 0, off_a = 0, off_s = 0, off_part = 0, bytes = 0;
 };
 
@@ -88,7 +88,10 @@ ForwardPlan plan_forward(const sv_model_desc& d, int M) {
     ForwardPlan p;
     p.M = M;
     p.kind = matmul_kind(d, M);
-    p.splits = p.kind == kMfmaTiled ? tiled_splits(M, d.d, d.ffn) : 0;
+    const int tiled = d.layout == SV_LAYOUT_TILED;
+    p.splits = p.kind == kMfmaTiled    ? tiled_splits(M, d.d, d.ffn)
+               : p.kind == kMfmaSkinny ? skinny_splits(M, d.d, d.ffn, tiled)
+                                       : 0;
     const int es = d.wdtype == SV_BF16 ? 2 : 4;
     size_t off = 0;
     p.off_h = off; off = align_up(off + (size_t)M * d.d * 4);
@@ -141,8 +144,8 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
         dn.act = act_s;
         dn.M = M; dn.N = d.d; dn.K = d.ffn;
         dn.epi = kEpiResidual; dn.bf16 = bf16; dn.tiled = tiled;
-        // the LDS-staged GEMM leaves split-K partial planes that the next norm
-        // folds in; the streaming kernels add into h directly
+        // with a K split the down projection leaves partial planes that the
+        // next norm folds in; otherwise it adds into h directly
         dn.out = p.splits ? static_cast<void*>(part) : static_cast<void*>(h);
         dn.splits = p.splits;
         e = launch_matmul(dn, p.kind, s);

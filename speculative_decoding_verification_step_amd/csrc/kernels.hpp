@@ -25,8 +25,9 @@ struct MatmulArgs {
     void* out;            // act_out (kEpiSilu), h (kEpiResidual) or f32_out (kEpiStore)
     int bf16;             // 1: bf16 weights/activations, 0: fp32
     int tiled;            // 1: W in the MFMA-tiled layout of pack.hip (bf16 only)
-    int splits;           // kMfmaTiled + kEpiResidual: K split count; `out` then
-                          // holds `splits` fp32 partial planes [M, N] (no add)
+    int splits;           // kEpiResidual on the MFMA kernels: K split count (0 = add
+                          // into h); `out` then holds `splits` fp32 partial
+                          // planes [M, N] that the next RMSNorm folds in
     const char* name;     // timing label, set by launch_matmul
 };
 
@@ -60,6 +61,8 @@ hipError_t launch_rmsnorm(const float* src, float* hout, const float* part, int 
 // Split count of the LDS-staged GEMM's K range for an [M, N, K] product
 // (so that the tile grid fills the chip).
 int tiled_splits(int M, int N, int K);
+// Split count of the streaming MFMA kernel's down projection (0: no split).
+int skinny_splits(int M, int N, int K, int tiled);
 
 // Softmax statistics at temperature T (1/T = inv_t), per chunk of
 // stats_chunks(V) chunks of each row: chunk max and sum of exp((z - max) / T)

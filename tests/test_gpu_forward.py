@@ -54,6 +54,23 @@ def test_small_bf16_forward_rows(M, tiled):
 
 
 @gpu
+@pytest.mark.parametrize("kind", ["skinny", "tiled"])
+@pytest.mark.parametrize("M", [17, 40, 64, 100])
+def test_bf16_forward_kernel_families(M, kind, monkeypatch):
+    """Both MFMA families at rows where either may run (the choice can be
+    forced for measurement); a long down projection makes both split K into
+    partial planes that the next norm folds in."""
+    sv = require_gpu()
+    monkeypatch.setenv("SPEC_VERIFY_MATMUL", kind)
+    w = workload.Workload("split-bf16", 512, 4096, 2, 1001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 2)
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w, M, sub=M)
+    z = cpu(m.forward(torch.from_numpy(h).cuda()))
+    _check(z, of.forward(model, h), TOL_BF16, f"split bf16 M={M} kind={kind}")
+
+
+@gpu
 @pytest.mark.parametrize("rows,cols,count", [(16, 32, 1), (1001, 256, 1), (48, 96, 3), (4096, 4096, 1)])
 def test_pack_matches_layout_definition(rows, cols, count):
     """The packed copy follows the documented tile order element by element."""

@@ -13,8 +13,10 @@ Prints ONE JSON line.  Default workload: the 8B-shaped stack at B=1, K=4
                     [--no-cpu-baseline] [--sweep]
 
 ``--sweep`` instead prints one JSON line per (B, K, sigma) point of the
-8B-shaped stack (B in 1,4,16,64; K in 1,2,4,8; sigma in 0.1, 0.5) plus the
-forward-only K=0 points, to locate the HBM -> MFMA crossover in B*(K+1).
+8B-shaped stack (B in 1,4,16,64; K in 1,2,4,8).  ``--crossover`` prints the
+forward-only time of each MFMA kernel family (weights streamed to registers
+vs LDS-staged GEMM) per row count, to locate the HBM -> MFMA crossover in
+B*(K+1).
 """
 from __future__ import annotations
 
@@ -36,6 +38,8 @@ METRIC = "verified positions/sec + accepted tokens/sec vs B,K; % HBM / % MFMA ro
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16
 VALU_F32_PEAK_TFS = 157.3
+# row counts B*(K+1) of the crossover scan (the sweep's B x K grid spans 2..576)
+CROSSOVER_ROWS = (16, 32, 48, 64, 80, 96, 128, 144, 192, 256, 320, 384, 512, 576, 768)
 
 
 def roofline_time_s(bytes_, flops, bw=HBM_PEAK_GBS * 1e9, peak=MFMA_BF16_PEAK_TFS * 1e12):
@@ -93,7 +97,12 @@ def _draft_tokens(zq, T, seed):
     return (zq / T - torch.log(-torch.log(u))).argmax(-1).to(torch.int32).contiguous()
 
 
-def _device_inputs(w, B, K, T, sigma, seed=0):
+_MODEL_CACHE: dict = {}
+
+
+def _device_models(w, sigma):
+    """Target model (packed once per process) and the drafter for `sigma`
+    (same blocks, head W_head + sigma * E)."""
     import torch
     import speculative_decoding_verification_step_amd as sv
 
@@ -102,27 +111,70 @@ def _device_inputs(w, B, K, T, sigma, seed=0):
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    model = workload.make_model(w, sigma=sigma)
-    d_up, d_down, d_gain = dev(model["w_up"]), dev(model["w_down"]), dev(model["gain"])
-    d_head, d_dhead = dev(model["w_head"]), dev(model["w_draft_head"])
-    host = {k: model[k] for k in ("w_up", "w_down", "gain", "w_head")}
-    del model
+    key = (w.name, sigma)
+    if _MODEL_CACHE.get("key") != key:
+        _MODEL_CACHE.clear()
+        torch.cuda.empty_cache()
+        model = workload.make_model(w, sigma=sigma)
+        d_up, d_down, d_gain = dev(model["w_up"]), dev(model["w_down"]), dev(model["gain"])
+        d_head, d_dhead = dev(model["w_head"]), dev(model["w_draft_head"])
+        host = {k: model[k] for k in ("w_up", "w_down", "gain", "w_head")}
+        del model
+        if w.wdtype == "bf16":
+            # the weights are packed once, at load time, into the tiled layout
+            target = sv.Model.packed(d_up, d_down, d_gain, d_head)
+            drafter = sv.Model.packed(d_up, d_down, d_gain, d_dhead)
+            del d_up, d_down
+        else:
+            target = sv.Model(d_up, d_down, d_gain, d_head)
+            drafter = sv.Model(d_up, d_down, d_gain, d_dhead)
+        _MODEL_CACHE.update(key=key, target=target, drafter=drafter, host=host)
+    return _MODEL_CACHE["target"], _MODEL_CACHE["drafter"], _MODEL_CACHE["host"]
+
+
+def _device_inputs(w, B, K, T, sigma, seed=0):
+    import torch
+    target, drafter, host = _device_models(w, sigma)
     M = B * (K + 1)
-    hidden = dev(workload.make_hidden(w, M))
-    if w.wdtype == "bf16":
-        # the weights are packed once, at load time, into the tiled layout
-        target = sv.Model.packed(d_up, d_down, d_gain, d_head)
-        drafter = sv.Model.packed(d_up, d_down, d_gain, d_dhead)
-        del d_up, d_down
-    else:
-        target = sv.Model(d_up, d_down, d_gain, d_head)
-        drafter = sv.Model(d_up, d_down, d_gain, d_dhead)
+    h = workload.make_hidden(w, M)
+    hidden = torch.from_numpy(h).cuda()
     # draft logits: the draft head reads the target's own final hidden state
     zq = drafter.forward(hidden).view(B, K + 1, w.vocab)[:, :K].contiguous()
     x = _draft_tokens(zq, T, seed)
-    del drafter, d_dhead
     torch.cuda.synchronize()
     return target, hidden, zq, x, host
+
+
+def _time_forward(target, hidden, steps, warmup):
+    """Milliseconds per forward (HIP graph replay) over `hidden`, in the
+    kernel family the library picks (or SPEC_VERIFY_MATMUL forces)."""
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    M = hidden.shape[0]
+    ws = sv.workspace(target.forward_workspace_bytes(M))
+    logits = torch.empty((M, target.vocab), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(warmup, 1)):
+            target.forward(hidden, logits, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            target.forward(hidden, logits, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay()
+        start.record(s)
+        for _ in range(steps):
+            g.replay()
+        stop.record(s)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    del g, ws, logits
+    return ms
 
 
 def _time_step(sv, target, hidden, zq, x, B, K, T, steps, warmup, use_graph, seed=0, stp=0):
@@ -310,6 +362,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--crossover", action="store_true",
+                    help="forward-only times of both MFMA kernel families over B*(K+1)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with one plain 256 MiB device copy (counter calibration)")
     a = ap.parse_args()
@@ -332,6 +386,26 @@ def main():
                     r = run_point(w, B, K, sigma, 1.0, max(20, a.steps // 4), 3, not a.eager,
                                   False, profile=False)
                     print(json.dumps(r), flush=True)
+        return
+    if a.crossover:
+        # forward-only time per row count with each MFMA family forced: the
+        # HBM-bound streaming kernel against the LDS-staged GEMM
+        import torch
+        w = workload.WORKLOADS["8b-shaped-sweep"]
+        target, _, _ = _device_models(w, w.sigma)
+        bytes_w = w.weight_elems() * 2
+        for M in CROSSOVER_ROWS:
+            hidden = torch.from_numpy(workload.make_hidden(w, M)).cuda()
+            row = {"crossover": w.name, "M": M}
+            for kind in ("skinny", "tiled"):
+                os.environ["SPEC_VERIFY_MATMUL"] = kind
+                ms = _time_forward(target, hidden, 20, 2)
+                row[kind] = {"ms": ms, "weight_TBps": bytes_w / (ms / 1e3) / 1e12,
+                             "TFLOPs": 2.0 * M * w.weight_elems() / (ms / 1e3) / 1e12}
+            os.environ.pop("SPEC_VERIFY_MATMUL", None)
+            row["auto_ms"] = _time_forward(target, hidden, 20, 2)
+            row["faster"] = min(("skinny", "tiled"), key=lambda k: row[k]["ms"])
+            print(json.dumps(row), flush=True)
         return
 
     w = workload.WORKLOADS[a.workload]

@@ -60,9 +60,11 @@ int forced_kind() {
     return k;
 }
 
-// Above this many rows the weights are reused from LDS (kMfmaTiled); up to it
-// every weight is streamed once per pass of 64 rows (kMfmaSkinny).
-constexpr int kTiledMinRows = 65;
+// From this many rows the weights are reused from LDS (kMfmaTiled); below it
+// every weight is streamed once per pass of 64 rows (kMfmaSkinny).  Measured
+// on the 8B-shaped stack: two streaming passes still beat the LDS-staged GEMM
+// at 128 rows (1.27 vs 1.79 ms per forward), the GEMM wins from 144.
+constexpr int kTiledMinRows = 136;
 
 int matmul_kind(const sv_model_desc& d, int M) {
     if (d.wdtype != SV_BF16) return kGemvValu;

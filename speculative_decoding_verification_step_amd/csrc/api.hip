@@ -61,10 +61,11 @@ int forced_kind() {
 }
 
 // From this many rows the weights are reused from LDS (kMfmaTiled); below it
-// every weight is streamed once per pass of 64 rows (kMfmaSkinny).  Measured
-// on the 8B-shaped stack: two streaming passes still beat the LDS-staged GEMM
-// at 128 rows (1.27 vs 1.79 ms per forward), the GEMM wins from 144.
-constexpr int kTiledMinRows = 136;
+// every weight is streamed once in a single pass (kMfmaSkinny, up to 64
+// rows).  Measured on the 8B-shaped stack: one streaming pass wins at 64 rows
+// (0.67 vs 0.90 ms per forward), the LDS-staged GEMM beats two passes from 80
+// rows on (0.91 vs 1.17 ms).
+constexpr int kTiledMinRows = 65;
 
 int matmul_kind(const sv_model_desc& d, int M) {
     if (d.wdtype != SV_BF16) return kGemvValu;
@@ -83,6 +84,7 @@ struct ForwardPlan {
     int M = 0;
     int kind = kGemvValu;
     int splits = 0;          // K splits (partial planes) of the down projection
+    int act_tiled = 0;       // bf16 activations in the operand layout (LDS-staged GEMM)
     size_t off_h = 0, off_a = 0, off_s = 0, off_part = 0, bytes = 0;
 };
 
@@ -94,11 +96,13 @@ ForwardPlan plan_forward(const sv_model_desc& d, int M) {
     p.splits = p.kind == kMfmaTiled    ? tiled_splits(M, d.d, d.ffn)
                : p.kind == kMfmaSkinny ? skinny_splits(M, d.d, d.ffn, tiled)
                                        : 0;
+    p.act_tiled = p.kind == kMfmaTiled;
     const int es = d.wdtype == SV_BF16 ? 2 : 4;
+    const size_t arows = p.act_tiled ? (size_t)(M + 15) / 16 * 16 : (size_t)M;
     size_t off = 0;
     p.off_h = off; off = align_up(off + (size_t)M * d.d * 4);
-    p.off_a = off; off = align_up(off + (size_t)M * d.d * es);
-    p.off_s = off; off = align_up(off + (size_t)M * d.ffn * es);
+    p.off_a = off; off = align_up(off + arows * d.d * es);
+    p.off_s = off; off = align_up(off + arows * d.ffn * es);
     p.off_part = off; off = align_up(off + (size_t)p.splits * M * d.d * 4);
     p.bytes = off;
     return p;
@@ -128,7 +132,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
     hipError_t e;
 
     // h <- hidden (the residual stream), a <- norm(h)
-    e = launch_rmsnorm(hidden, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, bf16, s);
+    e = launch_rmsnorm(hidden, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, bf16, p.act_tiled, s);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     for (int l = 0; l < d.n_layers; ++l) {
         // (ffn and d are multiples of 64, so the tiled matrices have the
@@ -138,6 +142,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
         up.act = a;
         up.M = M; up.N = d.ffn; up.K = d.d;
         up.epi = kEpiSilu; up.out = act_s; up.bf16 = bf16; up.tiled = tiled;
+        up.act_tiled = p.act_tiled;
         e = launch_matmul(up, p.kind, s);
         if (e != hipSuccess) return hip_fail(e, "up-projection launch");
 
@@ -146,6 +151,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
         dn.act = act_s;
         dn.M = M; dn.N = d.d; dn.K = d.ffn;
         dn.epi = kEpiResidual; dn.bf16 = bf16; dn.tiled = tiled;
+        dn.act_tiled = p.act_tiled;
         // with a K split the down projection leaves partial planes that the
         // next norm folds in; otherwise it adds into h directly
         dn.out = p.splits ? static_cast<void*>(part) : static_cast<void*>(h);
@@ -154,7 +160,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
         if (e != hipSuccess) return hip_fail(e, "down-projection launch");
 
         e = launch_rmsnorm(h, h, part, p.splits, d.gain + (size_t)(l + 1) * d.d, a, M, d.d,
-                           d.rms_eps, bf16, s);
+                           d.rms_eps, bf16, p.act_tiled, s);
         if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     }
     MatmulArgs hd{};
@@ -162,6 +168,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
     hd.act = a;
     hd.M = M; hd.N = d.vocab; hd.K = d.d;
     hd.epi = kEpiStore; hd.out = logits; hd.bf16 = bf16; hd.tiled = tiled;
+    hd.act_tiled = p.act_tiled;
     e = launch_matmul(hd, p.kind, s);
     if (e != hipSuccess) return hip_fail(e, "LM-head launch");
     return SV_OK;

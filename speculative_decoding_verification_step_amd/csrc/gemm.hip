@@ -6,16 +6,17 @@
 // reused across many activation rows from on-chip memory instead of being
 // streamed once per 64 rows.
 //
-// out^T tile [BN weight rows x BM activation rows] per workgroup.  Each k step
-// of 32, the workgroup's waves copy BN/16 weight blocks (1 KiB each, already in
-// matrix-core operand order in the tiled layout) and BM/16 activation blocks
-// (gathered per lane from the row-major activations into the same order)
-// straight from global memory into LDS with global_load_lds_dwordx4, through
-// a ring of NS stages (NS - 1 steps in flight).  Wave (wn, wm) then reads its
-// FN weight and FM activation operands from LDS (contiguous 1 KiB each, no
-// bank conflicts) and issues FN x FM v_mfma_f32_16x16x32_bf16.  The K range can
-// be split; split results go to fp32 partial planes that the following
-// RMSNorm folds in (in split order, so results are deterministic).
+// out^T tile [BN weight rows x BM activation rows] per workgroup.  Weights and
+// activations are both in the matrix-core operand layout (16 x 32 blocks of
+// one KiB in lane order; the activations are written that way, rows padded to
+// 16, by the RMSNorm and by this kernel's SiLU epilogue), so each k step of
+// 32 the workgroup's waves copy BN/16 + BM/16 contiguous KiB straight from
+// global memory into LDS with global_load_lds_dwordx4, through a ring of NS
+// stages (NS - 1 steps in flight).  Wave (wn, wm) then reads its FN weight
+// and FM activation operands from LDS (contiguous 1 KiB each, no bank
+// conflicts) and issues FN x FM v_mfma_f32_16x16x32_bf16.  The K range can be
+// split; split results go to fp32 partial planes that the following RMSNorm
+// folds in (in split order, so results are deterministic).
 //
 // Tile order: the grid is one-dimensional and workgroup i runs on XCD i % 8,
 // so tiles are renumbered to give every XCD a contiguous run, activation
@@ -73,30 +74,24 @@ __global__ __launch_bounds__(WN * WM * kWave, WPE) void mfma_tiled_kernel(
     const int s_end = min(S, s_begin + steps_per_split);
     const int nblk = (N + 15) / 16;              // weight blocks present in the tiled layout
 
-    // global source of this lane's 16 bytes for fragment f at step s
+    const int mblk = (M + 15) / 16;              // activation blocks (rows padded to 16)
+
+    // global source of this lane's 16 bytes for fragment f at step s: block
+    // row + 512 * s (weights and activations share the layout)
     const uint16_t* src[PER_WAVE];
-    int src_step[PER_WAVE];                      // element advance per k step
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
         const int f = wave + NW * i;
-        if (f < BNF) {
-            const int rb = min(nb0 + f, nblk - 1);
-            src[i] = Wt + (size_t)rb * S * 512 + lane * 8;
-            src_step[i] = 512;
-        } else {
-            const int m = min((mb0 + f - BNF) * 16 + (lane & 15), M - 1);
-            src[i] = act + (size_t)m * K + 8 * (lane >> 4);
-            src_step[i] = 32;
-        }
+        if (f < BNF) src[i] = Wt + (size_t)min(nb0 + f, nblk - 1) * S * 512 + lane * 8;
+        else src[i] = act + (size_t)min(mb0 + f - BNF, mblk - 1) * S * 512 + lane * 8;
     }
     auto issue = [&](int s) {
         const int st = (s - s_begin) % NS;
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int f = wave + NW * i;
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(src[i] + (size_t)src_step[i] * s),
-                (lds_void*)(&lds[st][f * 512]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)512 * s),
+                                             (lds_void*)(&lds[st][f * 512]), 16, 0, 0);
         }
     };
 
@@ -135,63 +130,61 @@ __global__ __launch_bounds__(WN * WM * kWave, WPE) void mfma_tiled_kernel(
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
 
-    // epilogue: lane holds rows n = base + 4*(lane/16) + r, column m = lane % 16
+    // epilogue: lane holds rows n = base + 4*(lane/16) + r, column m = lane % 16.
+    // The SiLU output (next matmul's activations) is written in the operand
+    // layout over all padded rows; the fp32 outputs row-major for m < M.
+    const int mpad = mblk * 16;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
         const int n = (nb0 + wn * FN + i) * 16 + 4 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int m = (mb0 + wm * FM + j) * 16 + (lane & 15);
+            const f32x4v v = acc[i][j];
+            if constexpr (EPI == kEpiSilu) {
+                // N % 32 == 0: the four outputs are 8 contiguous bytes of one block
+                if (m >= mpad || n >= N) continue;
+                const size_t o = ((size_t)(m >> 4) * (N >> 5) + (n >> 5)) * 512 +
+                                 ((m & 15) + 16 * ((n & 31) >> 3)) * 8 + (n & 7);
+                uint2 pk;
+                pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
+                pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = pk;
+                continue;
+            }
             if (m >= M) continue;
+            float* dst = static_cast<float*>(out) + (EPI == kEpiResidual ? split * split_stride : 0);
             const size_t o0 = (size_t)m * N + n;
             if (n + 3 < N && (N & 3) == 0) {
-                // four consecutive outputs of one row: one vector store
-                const f32x4v v = acc[i][j];
-                if constexpr (EPI == kEpiSilu) {
-                    uint2 pk;
-                    pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
-                    pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o0) = pk;
-                } else if constexpr (EPI == kEpiResidual) {
-                    *reinterpret_cast<f32x4v*>(static_cast<float*>(out) + split * split_stride + o0) = v;
-                } else {
-                    *reinterpret_cast<f32x4v*>(static_cast<float*>(out) + o0) = v;
-                }
+                *reinterpret_cast<f32x4v*>(dst + o0) = v;   // four consecutive outputs of one row
                 continue;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (n + r >= N) break;
-                const float v = acc[i][j][r];
-                const size_t o = (size_t)m * N + n + r;
-                if constexpr (EPI == kEpiSilu) {
-                    static_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(silu(v));
-                } else if constexpr (EPI == kEpiResidual) {
-                    static_cast<float*>(out)[split * split_stride + o] = v;   // partial plane
-                } else {
-                    static_cast<float*>(out)[o] = v;
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) dst[o0 + r] = v[r];
         }
     }
 }
 
-// Tile shapes (measured at 768 rows on the 8B-shaped matrices):
-//  large  - 2 x 4 waves of 128 x 64: 256 x 256 tiles, 3 stages of 32 KiB, one
-//           workgroup per CU; for grids of many tiles (the LM head)
-//  medium - 2 x 2 waves of 128 x 64: 256 x 128 tiles, 2 stages of 24 KiB, up to
-//           three workgroups per CU; for grids of a few hundred tiles
+// Tile shapes (measured at 256, 384 and 768 rows on the 8B-shaped matrices,
+// random operands, weights not cache-resident):
+//  small - 2 x 2 waves of 64 x 64: 128 x 128 tiles, 3 stages of 16 KiB; the up
+//          projection (no K split, so it needs many tiles)
+//  wide  - 4 x 2 waves of 64 x 64: 256 x 128 tiles, 3 stages of 24 KiB, two
+//          workgroups per CU; the down projection (with a K split) and the LM
+//          head when it has many tiles
+//  large - 2 x 4 waves of 128 x 64: 256 x 256 tiles, 4 stages of 32 KiB, one
+//          workgroup per CU; the LM head at a few hundred rows
 // (WPE: waves per SIMD the register allocation must allow)
-struct TileLarge { static constexpr int WN = 2, WM = 4, FN = 8, FM = 4, NS = 3, WPE = 2; };
-struct TileMedium { static constexpr int WN = 2, WM = 2, FN = 8, FM = 4, NS = 2, WPE = 2; };
+struct TileSmall { static constexpr int WN = 2, WM = 2, FN = 4, FM = 4, NS = 3, WPE = 2; };
+struct TileWide { static constexpr int WN = 4, WM = 2, FN = 4, FM = 4, NS = 3, WPE = 2; };
+struct TileLarge { static constexpr int WN = 2, WM = 4, FN = 8, FM = 4, NS = 4, WPE = 2; };
 
 template <class T> constexpr int tile_n() { return T::WN * T::FN * 16; }
 template <class T> constexpr int tile_m() { return T::WM * T::FM * 16; }
 template <class T> long long tile_count(int M, int N) {
     return (long long)((N + tile_n<T>() - 1) / tile_n<T>()) * ((M + tile_m<T>() - 1) / tile_m<T>());
 }
-
-bool use_large(int M, int N) { return tile_count<TileLarge>(M, N) >= 512; }
 
 template <class T>
 int splits_for(int M, int N, int K) {
@@ -204,9 +197,7 @@ int splits_for(int M, int N, int K) {
 
 }  // namespace
 
-int tiled_splits(int M, int N, int K) {
-    return use_large(M, N) ? splits_for<TileLarge>(M, N, K) : splits_for<TileMedium>(M, N, K);
-}
+int tiled_splits(int M, int N, int K) { return splits_for<TileWide>(M, N, K); }
 
 namespace {
 
@@ -226,17 +217,23 @@ hipError_t launch_tile(const MatmulArgs& a, int splits, hipStream_t stream) {
 
 template <int EPI>
 hipError_t launch_epi(const MatmulArgs& a, hipStream_t stream) {
-    // only the down projection (residual epilogue) may split K; its split
-    // count sizes the caller's partial planes
-    const int splits = EPI == kEpiResidual && a.splits > 0 ? a.splits : 1;
-    return use_large(a.M, a.N) ? launch_tile<TileLarge, EPI>(a, splits, stream)
-                               : launch_tile<TileMedium, EPI>(a, splits, stream);
+    if constexpr (EPI == kEpiSilu) {
+        return launch_tile<TileSmall, EPI>(a, 1, stream);
+    } else if constexpr (EPI == kEpiResidual) {
+        // only the down projection splits K; its split count sizes the
+        // caller's partial planes (tiled_splits)
+        return launch_tile<TileWide, EPI>(a, a.splits > 0 ? a.splits : 1, stream);
+    } else {
+        return tile_count<TileWide>(a.M, a.N) >= 1200 ? launch_tile<TileWide, EPI>(a, 1, stream)
+                                                      : launch_tile<TileLarge, EPI>(a, 1, stream);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_mfma_tiled(const MatmulArgs& a, hipStream_t stream) {
-    if (!a.bf16 || !a.tiled || a.K % 32) return hipErrorInvalidValue;
+    if (!a.bf16 || !a.tiled || !a.act_tiled || a.K % 32) return hipErrorInvalidValue;
+    if (a.epi == kEpiSilu && a.N % 32) return hipErrorInvalidValue;
     switch (a.epi) {
         case kEpiSilu: return launch_epi<kEpiSilu>(a, stream);
         case kEpiResidual: return launch_epi<kEpiResidual>(a, stream);

@@ -25,6 +25,8 @@ struct MatmulArgs {
     void* out;            // act_out (kEpiSilu), h (kEpiResidual) or f32_out (kEpiStore)
     int bf16;             // 1: bf16 weights/activations, 0: fp32
     int tiled;            // 1: W in the MFMA-tiled layout of pack.hip (bf16 only)
+    int act_tiled;        // 1: `act` (and the kEpiSilu output) in the operand layout of
+                          // the tiled weights, rows padded to 16 (kMfmaTiled only)
     int splits;           // kEpiResidual on the MFMA kernels: K split count (0 = add
                           // into h); `out` then holds `splits` fp32 partial
                           // planes [M, N] that the next RMSNorm folds in
@@ -53,10 +55,11 @@ double matmul_bytes(const MatmulArgs& a, int rows);
 // with h = src + part[0] + ... + part[splits-1] (split-K planes of [M, d],
 // none when splits == 0); h is written to hout when hout != src or partials
 // were folded (the first block copies the caller's hidden states into the
-// residual stream).
+// residual stream).  act_tiled (bf16): act in the operand layout of the tiled
+// weights, rows padded to a multiple of 16 with zeros.
 hipError_t launch_rmsnorm(const float* src, float* hout, const float* part, int splits,
                           const float* gain, void* act, int M, int d, float eps, int bf16,
-                          hipStream_t stream);
+                          int act_tiled, hipStream_t stream);
 
 // Split count of the LDS-staged GEMM's K range for an [M, N, K] product
 // (so that the tile grid fills the chip).

@@ -4,12 +4,14 @@
 One step = spec_verify_step over one batch: the target forward over all
 B*(K+1) positions (weights streamed once) plus rejection sampling.  Inputs
 (weights, hidden states, draft logits, draft tokens) are synthetic and
-resident in HBM before timing starts; the step is replayed from a HIP graph.
+resident in HBM before timing starts.  The steps are launched eagerly,
+back to back on one stream (measured faster than HIP graph replay on this
+stack: about 1 us per graph node); the graph-replay time is reported too.
 
 Prints ONE JSON line.  Default workload: the 8B-shaped stack at B=1, K=4
 (d=4096, ffn=14336, L=8, V=32000, bf16, sigma=0.3, T=1).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
                     [--no-cpu-baseline] [--sweep]
 
 ``--sweep`` instead prints one JSON line per (B, K, sigma) point of the
@@ -145,35 +147,63 @@ def _device_inputs(w, B, K, T, sigma, seed=0):
     return target, hidden, zq, x, host
 
 
-def _time_forward(target, hidden, steps, warmup):
-    """Milliseconds per forward (HIP graph replay) over `hidden`, in the
-    kernel family the library picks (or SPEC_VERIFY_MATMUL forces)."""
+def _time_fn(fn, steps, warmup, use_graph):
+    """Milliseconds per call of fn(stream): `steps` calls launched back to back
+    (or one call captured in a HIP graph and replayed `steps` times) between
+    two events."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(warmup, 1)):
+            fn(s)
+    torch.cuda.synchronize()
+    g = None
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                fn(s)
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay() if g is not None else fn(s)
+        start.record(s)
+        for _ in range(steps):
+            g.replay() if g is not None else fn(s)
+        stop.record(s)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    del g
+    return ms
+
+
+def _time_forward(target, hidden, steps, warmup, use_graph=False):
+    """Milliseconds per forward over `hidden`, in the kernel family the
+    library picks (or SPEC_VERIFY_MATMUL forces)."""
     import torch
     import speculative_decoding_verification_step_amd as sv
     M = hidden.shape[0]
     ws = sv.workspace(target.forward_workspace_bytes(M))
     logits = torch.empty((M, target.vocab), dtype=torch.float32, device="cuda")
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(max(warmup, 1)):
-            target.forward(hidden, logits, ws=ws, stream=s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            target.forward(hidden, logits, ws=ws, stream=s)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        g.replay()
-        start.record(s)
-        for _ in range(steps):
-            g.replay()
-        stop.record(s)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
-    del g, ws, logits
+    ms = _time_fn(lambda s: target.forward(hidden, logits, ws=ws, stream=s), steps, warmup,
+                  use_graph)
+    del ws, logits
+    return ms
+
+
+def _time_accept(logits, zq, x, B, K, T, steps, warmup, use_graph=False):
+    """Milliseconds per rejection-sampling call alone."""
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    V = logits.shape[1]
+    ws = sv.workspace(sv.accept_workspace_bytes(B, K, V))
+    out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    tl = logits.view(B, K + 1, V)
+    ms = _time_fn(lambda s: sv.accept(tl, zq if T > 0 else None, x, T, 0, 0, out_tokens=out,
+                                      accept_len=al, ws=ws, stream=s), steps, warmup, use_graph)
+    del ws, out, al
     return ms
 
 
@@ -292,6 +322,14 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
         als.append(al.cpu().numpy().copy())
     als = np.concatenate(als)
     bytes_, flops = step_work(w, B, K, T)
+    # the two halves alone (same launch mode), and the step in the other mode
+    sub = max(10, steps // 4)
+    fwd_ms = _time_forward(target, hidden, sub, 2, use_graph)
+    acc_ms = _time_accept(logits, zq, x, B, K, T, sub, 2, use_graph)
+    other_ms, _, other_per, _ = _time_step(sv, target, hidden, zq, x, B, K, T, sub, 2,
+                                           not use_graph)
+    es = 2 if w.wdtype == "bf16" else 4
+    fwd_bytes = w.weight_elems() * es + (w.n_layers + 1) * w.d * 4 + M * w.d * 4 + M * w.vocab * 4
     res = {
         "metric": METRIC,
         "value": M / (ms / 1e3),
@@ -318,6 +356,14 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
         "step_hbm_frac": bytes_ / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
         "step_mfma_frac": flops / (ms / 1e3) / (MFMA_BF16_PEAK_TFS * 1e12),
         "roofline_step_ms": roofline_time_s(bytes_, flops) * 1e3,
+        "forward_ms": fwd_ms,
+        "forward_hbm_frac": fwd_bytes / (fwd_ms / 1e3) / (HBM_PEAK_GBS * 1e9),
+        "forward_mfma_frac": flops / (fwd_ms / 1e3) / (MFMA_BF16_PEAK_TFS * 1e12),
+        "accept_ms": acc_ms,
+        ("eager_ms_per_step" if use_graph else "graph_ms_per_step"): other_ms,
+        ("eager_step_ms_p10_p50_p90" if use_graph else "graph_step_ms_p10_p50_p90"):
+            [other_per[len(other_per) // 10], other_per[len(other_per) // 2],
+             other_per[(9 * len(other_per)) // 10]],
     }
     if profile:
         kt = _profile_kernels(sv, one, s, reps=5)
@@ -348,6 +394,55 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
     return res
 
 
+K_TABLE_B = (1, 4, 16, 64)
+K_TABLE_K = tuple(range(9))
+K_TABLE_CHOOSE_B = (1, 2, 4, 8, 16, 32, 64)
+K_TABLE_DRAFT_C = (0.0, 0.05)
+
+
+def _k_table(a):
+    """Hardware-aware draft length: the verification step is timed on this GPU
+    at every B x K of the sweep grid (rows M = B (K + 1)), AL(K) is measured
+    on the same synthetic drafts, and the library picks the K of highest
+    goodput AL / (T_verif + T_draft) per batch size, for a free draft and for
+    a draft costing c * T_verif(B) per token."""
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    w = workload.WORKLOADS["8b-shaped-sweep"]
+    for sigma in workload.SWEEP_SIGMA:
+        times: dict = {}
+        al = [1.0]
+        for K in K_TABLE_K:
+            for B in K_TABLE_B:
+                target, hidden, zq, x, _ = _device_inputs(w, B, K, 1.0, sigma)
+                ms, _, _, (logits, out, alb, ws, _, _) = _time_step(
+                    sv, target, hidden, zq, x, B, K, 1.0, 20, 2, a.graph)
+                times.setdefault(B * (K + 1), []).append(ms)
+                if B == K_TABLE_B[-1] and K > 0:
+                    als = []
+                    for stp in range(16):
+                        xs = _draft_tokens(zq, 1.0, 2000 + stp)
+                        target.step(hidden, zq, xs, B, K, 1.0, 0, stp, logits, out, alb, ws=ws)
+                        als.append(alb.cpu().numpy().copy())
+                    al.append(float(np.concatenate(als).mean()))
+                del hidden, zq, x, logits, out, alb, ws
+                torch.cuda.synchronize()
+        m_rows = sorted(times)
+        t_verif = [float(np.mean(times[m])) for m in m_rows]
+        res = {"k_table": w.name, "sigma": sigma, "temperature": 1.0,
+               "launch": "hipgraph" if a.graph else "eager",
+               "al_measured": al, "rows": m_rows, "t_verif_ms": t_verif, "choice": {}}
+        for c in K_TABLE_DRAFT_C:
+            t_b = {B: float(np.interp(B, m_rows, t_verif)) for B in K_TABLE_CHOOSE_B}
+            draft = [[c * K * t_b[B] for K in K_TABLE_K] for B in K_TABLE_CHOOSE_B]
+            k, g = sv.choose_k(m_rows, t_verif, al, list(K_TABLE_CHOOSE_B), draft)
+            res["choice"][f"c={c}"] = {
+                str(B): {"K": int(k[i]), "goodput_tokens_per_ms_per_request": float(g[i]),
+                         "speedup_vs_K0": float(g[i] * t_b[B])}
+                for i, B in enumerate(K_TABLE_CHOOSE_B)}
+        print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,10 +453,16 @@ def main():
     ap.add_argument("--K", type=int)
     ap.add_argument("--sigma", type=float)
     ap.add_argument("--T", type=float)
-    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP graph replays as the headline (default: eager launches; the "
+                         "other mode is reported beside it)")
+    ap.add_argument("--eager", action="store_true", help=argparse.SUPPRESS)  # the default
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--k-table", action="store_true",
+                    help="measure T_verif(M) and AL(K) on the sweep stack and print the "
+                         "goodput-optimal draft length per batch size")
     ap.add_argument("--crossover", action="store_true",
                     help="forward-only times of both MFMA kernel families over B*(K+1)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -383,9 +484,12 @@ def main():
         for sigma in workload.SWEEP_SIGMA:
             for B in workload.SWEEP_B:
                 for K in workload.SWEEP_K:
-                    r = run_point(w, B, K, sigma, 1.0, max(20, a.steps // 4), 3, not a.eager,
+                    r = run_point(w, B, K, sigma, 1.0, max(20, a.steps // 4), 3, a.graph,
                                   False, profile=False)
                     print(json.dumps(r), flush=True)
+        return
+    if a.k_table:
+        _k_table(a)
         return
     if a.crossover:
         # forward-only time per row count with each MFMA family forced: the
@@ -413,7 +517,7 @@ def main():
     K = w.K if a.K is None else a.K
     sigma = w.sigma if a.sigma is None else a.sigma
     T = w.temperature if a.T is None else a.T
-    res = run_point(w, B, K, sigma, T, a.steps, a.warmup, not a.eager, not a.no_cpu_baseline,
+    res = run_point(w, B, K, sigma, T, a.steps, a.warmup, a.graph, not a.no_cpu_baseline,
                     profile=not a.no_profile)
     print(json.dumps(res), flush=True)
     if a.calib_copy:

@@ -10,6 +10,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +63,8 @@ EXPORTS = {
     "spec_verify_profile_begin": (ctypes.c_int, [_i32]),
     "spec_verify_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), _i32,
                                                ctypes.POINTER(_i32)]),
+    "spec_verify_choose_k": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "spec_verify_window_k": (_i32, [_vp, _i32, _i32, ctypes.c_float, _i32, _i32]),
 }
 
 _lib = None
@@ -292,3 +296,35 @@ def profile_end(cap: int = 64):
     _check(lib().spec_verify_profile_end(arr, cap, ctypes.byref(n)))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms, arr[i].bytes, arr[i].flops)
             for i in range(min(n.value, cap))}
+
+
+def choose_k(m_rows, t_verif, al, batch, t_draft=None):
+    """Goodput-optimal draft length per batch size (host arrays; see
+    include/spec_verify_kselect.h).  Returns (k [n_b] int32, goodput [n_b])."""
+    m = np.ascontiguousarray(m_rows, dtype=np.int32)
+    t = np.ascontiguousarray(t_verif, dtype=np.float64)
+    a = np.ascontiguousarray(al, dtype=np.float64)
+    b = np.ascontiguousarray(batch, dtype=np.int32)
+    d = None if t_draft is None else np.ascontiguousarray(t_draft, dtype=np.float64)
+    if d is not None and d.shape != (len(b), len(a)):
+        raise ValueError(f"t_draft must be [{len(b)}, {len(a)}], got {d.shape}")
+    if len(t) != len(m):
+        raise ValueError("m_rows and t_verif differ in length")
+    k = np.empty(len(b), np.int32)
+    g = np.empty(len(b), np.float64)
+    _check(lib().spec_verify_choose_k(m.ctypes.data, t.ctypes.data, len(m), a.ctypes.data, len(a),
+                                      b.ctypes.data, len(b),
+                                      None if d is None else d.ctypes.data,
+                                      k.ctypes.data, g.ctypes.data))
+    return k, g
+
+
+def window_k(accept_len, window: int = 10, threshold: float = 1.5, k_high: int = 5,
+             k_low: int = 2) -> int:
+    """Speculation window from recent acceptance lengths (host array)."""
+    a = np.ascontiguousarray(accept_len, dtype=np.int32)
+    r = int(lib().spec_verify_window_k(a.ctypes.data if len(a) else None, len(a), window,
+                                       float(threshold), k_high, k_low))
+    if r < 0:
+        _check(r)
+    return r

@@ -15,6 +15,7 @@
 #include <string>
 #include <vector>
 
+#include "host.hpp"
 #include "kernels.hpp"
 #include "spec_verify.h"
 
@@ -23,9 +24,10 @@ struct sv_model {
 };
 
 namespace sv {
-namespace {
 
+namespace {
 thread_local std::string g_err;
+}  // namespace
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -36,6 +38,8 @@ int fail(int code, const char* fmt, ...) {
     g_err = buf;
     return code;
 }
+
+namespace {
 
 int hip_fail(hipError_t e, const char* what) {
     return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

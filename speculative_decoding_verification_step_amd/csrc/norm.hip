@@ -48,11 +48,15 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     }
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src + off);
 
-    f32x4 h[VPT];
+    // the row and the gains are loaded together, so the gains do not add a
+    // second memory round trip after the reduction
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(gain);
+    f32x4 h[VPT], g[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = tid + v * THREADS;
         h[v] = c < n4 ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        g[v] = c < n4 ? g4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (splits > 0) {
 #pragma unroll
@@ -91,14 +95,12 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     for (int w = 0; w < THREADS / kWave; ++w) tot += red[w];
     const float inv_rms = 1.0f / sqrtf(tot / (float)d + eps);
 
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(gain);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = tid + v * THREADS;
         if (c >= n4) continue;
-        const f32x4 g = g4[c];
-        const f32x4 y = {h[v].x * inv_rms * g.x, h[v].y * inv_rms * g.y, h[v].z * inv_rms * g.z,
-                         h[v].w * inv_rms * g.w};
+        const f32x4 y = {h[v].x * inv_rms * g[v].x, h[v].y * inv_rms * g[v].y,
+                         h[v].z * inv_rms * g[v].z, h[v].w * inv_rms * g[v].w};
         if constexpr (kBf16) {
             uint2 packed;
             packed.x = f32_to_bf16(y.x) | (f32_to_bf16(y.y) << 16);

@@ -1,6 +1,7 @@
 """The C ABI library loads, exports every declared symbol, and rejects bad
 arguments on the host before touching the GPU (no compute calls here)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -10,7 +11,7 @@ import pytest
 from speculative_decoding_verification_step_amd import binding as bd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 FAKE = 0x10000  # a non-null, aligned address; never dereferenced by the host checks
 
 
@@ -22,7 +23,7 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)
     return sorted(set(n for n in names if n not in ("if", "defined")))
@@ -32,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify_forward", "spec_verify_accept", "spec_verify_step",
               "sv_model_create", "sv_model_destroy", "spec_verify_workspace_bytes",
-              "spec_verify_last_error"):
+              "spec_verify_last_error", "spec_verify_choose_k", "spec_verify_window_k"):
         assert n in names
 
 

@@ -166,16 +166,25 @@ __global__ __launch_bounds__(WN * WM * kWave, WPE) void mfma_tiled_kernel(
     }
 }
 
-// Tile shapes (measured at 256, 384 and 768 rows on the 8B-shaped matrices,
-// random operands, weights not cache-resident):
+// Tile shapes (measured at 80 - 768 rows on the 8B-shaped matrices and the
+// large-batch LM head, random operands, weights not cache-resident):
+//  thin  - 2 x 2 waves of 32 x 32: 64 x 64 tiles, 3 stages of 8 KiB; the up
+//          projection up to 128 rows (it cannot split K, so it needs narrow
+//          tiles for enough workgroups)
+//  tall  - 2 x 2 waves of 32 x 64: 64 x 128 tiles, 3 stages of 12 KiB; the up
+//          projection at 129 - 256 rows
 //  small - 2 x 2 waves of 64 x 64: 128 x 128 tiles, 3 stages of 16 KiB; the up
-//          projection (no K split, so it needs many tiles)
+//          projection above 256 rows, the down projection (K split) and the
+//          LM head up to 128 rows
 //  wide  - 4 x 2 waves of 64 x 64: 256 x 128 tiles, 3 stages of 24 KiB, two
-//          workgroups per CU; the down projection (with a K split) and the LM
-//          head when it has many tiles
+//          workgroups per CU; the down projection above 128 rows and the LM
+//          head with many tiles
 //  large - 2 x 4 waves of 128 x 64: 256 x 256 tiles, 4 stages of 32 KiB, one
-//          workgroup per CU; the LM head at a few hundred rows
+//          workgroup per CU; the LM head of a large vocabulary at a few
+//          hundred rows
 // (WPE: waves per SIMD the register allocation must allow)
+struct TileThin { static constexpr int WN = 2, WM = 2, FN = 2, FM = 2, NS = 3, WPE = 2; };
+struct TileTall { static constexpr int WN = 2, WM = 2, FN = 2, FM = 4, NS = 3, WPE = 2; };
 struct TileSmall { static constexpr int WN = 2, WM = 2, FN = 4, FM = 4, NS = 3, WPE = 2; };
 struct TileWide { static constexpr int WN = 4, WM = 2, FN = 4, FM = 4, NS = 3, WPE = 2; };
 struct TileLarge { static constexpr int WN = 2, WM = 4, FN = 8, FM = 4, NS = 4, WPE = 2; };
@@ -195,9 +204,14 @@ int splits_for(int M, int N, int K) {
     return splits;
 }
 
+// The down projection's tile: 128 x 128 up to 128 rows, 256 x 128 above.
+bool down_small(int M) { return M <= 128; }
+
 }  // namespace
 
-int tiled_splits(int M, int N, int K) { return splits_for<TileWide>(M, N, K); }
+int tiled_splits(int M, int N, int K) {
+    return down_small(M) ? splits_for<TileSmall>(M, N, K) : splits_for<TileWide>(M, N, K);
+}
 
 namespace {
 
@@ -218,14 +232,20 @@ hipError_t launch_tile(const MatmulArgs& a, int splits, hipStream_t stream) {
 template <int EPI>
 hipError_t launch_epi(const MatmulArgs& a, hipStream_t stream) {
     if constexpr (EPI == kEpiSilu) {
+        if (a.M <= 128) return launch_tile<TileThin, EPI>(a, 1, stream);
+        if (a.M <= 256) return launch_tile<TileTall, EPI>(a, 1, stream);
         return launch_tile<TileSmall, EPI>(a, 1, stream);
     } else if constexpr (EPI == kEpiResidual) {
         // only the down projection splits K; its split count sizes the
-        // caller's partial planes (tiled_splits)
-        return launch_tile<TileWide, EPI>(a, a.splits > 0 ? a.splits : 1, stream);
+        // caller's partial planes (tiled_splits, same tile rule)
+        const int splits = a.splits > 0 ? a.splits : 1;
+        return down_small(a.M) ? launch_tile<TileSmall, EPI>(a, splits, stream)
+                               : launch_tile<TileWide, EPI>(a, splits, stream);
     } else {
-        return tile_count<TileWide>(a.M, a.N) >= 1200 ? launch_tile<TileWide, EPI>(a, 1, stream)
-                                                      : launch_tile<TileLarge, EPI>(a, 1, stream);
+        if (a.M <= 128) return launch_tile<TileSmall, EPI>(a, 1, stream);
+        if (tile_count<TileWide>(a.M, a.N) >= 1200) return launch_tile<TileWide, EPI>(a, 1, stream);
+        if (tile_count<TileLarge>(a.M, a.N) >= 400) return launch_tile<TileLarge, EPI>(a, 1, stream);
+        return launch_tile<TileWide, EPI>(a, 1, stream);
     }
 }
 

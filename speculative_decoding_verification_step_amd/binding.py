@@ -64,6 +64,17 @@ EXPORTS = {
     "spec_verify_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), _i32,
                                                ctypes.POINTER(_i32)]),
     "spec_verify_choose_k": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "spec_verify_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "spec_verify_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _vp]),
+    "spec_verify_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "spec_verify_kv_commit": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
+    "sv_kv_pool_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
+    "sv_kv_pool_destroy": (None, [_vp]),
+    "sv_kv_pool_free_blocks": (_i32, [_vp]),
+    "sv_kv_pool_reserve": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32]),
+    "sv_kv_pool_trim": (ctypes.c_int, [_vp, _vp, _vp, _i32]),
     "spec_verify_window_k": (_i32, [_vp, _i32, _i32, ctypes.c_float, _i32, _i32]),
 }
 
@@ -328,3 +339,97 @@ def window_k(accept_len, window: int = 10, threshold: float = 1.5, k_high: int =
     if r < 0:
         _check(r)
     return r
+
+
+# ---- paged attention of the verified positions (include/spec_verify_attn.h) ----
+KV_BLOCK = 32
+
+
+def _bf16(t, name, shape):
+    _need(t, name, torch.bfloat16, shape)
+
+
+def attention_workspace_bytes(B: int, T: int, Hq: int, Hkv: int, head_dim: int,
+                              max_blocks: int) -> int:
+    return int(lib().spec_verify_attention_workspace_bytes(B, T, Hq, Hkv, head_dim, max_blocks))
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, ctx_len, stream=None):
+    """Write k_new / v_new [B, T, Hkv, Dh] (bf16) at positions ctx_len[b] + t."""
+    B, T, Hkv, Dh = k_new.shape
+    nb = k_cache.shape[0]
+    mb = block_table.shape[1]
+    _bf16(k_new, "k_new", (B, T, Hkv, Dh))
+    _bf16(v_new, "v_new", (B, T, Hkv, Dh))
+    _bf16(k_cache, "k_cache", (nb, Hkv, KV_BLOCK, Dh))
+    _bf16(v_cache, "v_cache", (nb, Hkv, Dh, KV_BLOCK))
+    _need(block_table, "block_table", torch.int32, (B, mb))
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    _check(lib().spec_verify_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_table), _ptr(ctx_len), B, T, Hkv, Dh, mb, nb,
+                                       _stream(stream)))
+
+
+def attention(q, k_cache, v_cache, block_table, ctx_len, scale: float, out=None, ws=None,
+              stream=None):
+    """Causal attention of q [B, T, Hq, Dh] (bf16) over the paged cache;
+    returns out [B, T, Hq, Dh] fp32."""
+    B, T, Hq, Dh = q.shape
+    nb, Hkv = k_cache.shape[:2]
+    mb = block_table.shape[1]
+    _bf16(q, "q", (B, T, Hq, Dh))
+    _bf16(k_cache, "k_cache", (nb, Hkv, KV_BLOCK, Dh))
+    _bf16(v_cache, "v_cache", (nb, Hkv, Dh, KV_BLOCK))
+    _need(block_table, "block_table", torch.int32, (B, mb))
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, T, Hq, Dh), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, T, Hq, Dh))
+    if ws is None:
+        n = attention_workspace_bytes(B, T, Hq, Hkv, Dh, mb)
+        ws = workspace(n, q.device) if n else None
+    _check(lib().spec_verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(ctx_len), B, T, Hq, Hkv, Dh, mb, nb, float(scale),
+                                       _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(stream)))
+    return out
+
+
+def kv_commit(ctx_len, accept_len, stream=None):
+    """ctx_len[b] += accept_len[b] (AL >= 1) on the device."""
+    B = ctx_len.shape[0]
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _check(lib().spec_verify_kv_commit(_ptr(ctx_len), _ptr(accept_len), B, _stream(stream)))
+
+
+class KVPool:
+    """Host free list of physical KV blocks (sv_kv_pool)."""
+
+    def __init__(self, num_blocks: int):
+        h = _vp()
+        _check(lib().sv_kv_pool_create(num_blocks, ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.sv_kv_pool_destroy(self._h)
+            self._h = None
+
+    @property
+    def free_blocks(self) -> int:
+        return int(lib().sv_kv_pool_free_blocks(self._h))
+
+    def reserve(self, row: np.ndarray, n_blocks: int, tokens: int) -> int:
+        """Grow a host int32 table row (n_blocks in use) to cover `tokens`."""
+        assert row.dtype == np.int32 and row.flags.c_contiguous
+        n = _i32(n_blocks)
+        _check(lib().sv_kv_pool_reserve(self._h, row.ctypes.data, ctypes.byref(n), len(row), tokens))
+        return n.value
+
+    def trim(self, row: np.ndarray, n_blocks: int, tokens: int) -> int:
+        """Return the row's blocks past `tokens` positions; the new count."""
+        assert row.dtype == np.int32 and row.flags.c_contiguous
+        n = _i32(n_blocks)
+        _check(lib().sv_kv_pool_trim(self._h, row.ctypes.data, ctypes.byref(n), tokens))
+        return n.value

@@ -20,8 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "gemm.hip", "kselect.cpp", "matmul.hip", "gemv.hip", "mfma.hip", "norm.hip", "pack.hip",
-           "vocab.hip"]
+SOURCES = ["api.hip", "attn.hip", "gemm.hip", "kselect.cpp", "kvpool.cpp", "matmul.hip", "gemv.hip",
+           "mfma.hip", "norm.hip", "pack.hip", "vocab.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

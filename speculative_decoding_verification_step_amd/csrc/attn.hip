@@ -1,0 +1,402 @@
+// Causal attention of the T = K + 1 verified positions over a paged KV cache,
+// the append of their keys/values, and the commit after acceptance (C ABI in
+// include/spec_verify_attn.h).
+//
+// The target scores every drafted slot in one pass (NVIDIA co-design post,
+// "What is speculative decoding?"; its "Draft length and attention
+// performance": with G query heads per KV head the attention GEMM-M is
+// G (1 + D)).  One wave owns 16 of the G*T query rows of one (request, KV
+// head) and one range of KV blocks; both products run on the matrix cores
+// with the keys as the row dimension:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims of a block
+//                 (contiguous in k_cache), B = Q^T (each lane's query row);
+//   O^T += V^T P^T  A = V^T (16 dims x 32 keys; V is stored transposed per
+//                 block), B = P^T.
+// In the MFMA output layout a lane holds four keys of S^T for one query row,
+// and its eight probabilities (two key tiles) are exactly the B operand of
+// the second product once the 32 k slots are ordered (keys 4g..4g+3 of tile
+// 0, then keys 16+4g..16+4g+3 of tile 1) - the A operand V^T uses the same
+// order - so the softmax needs no transpose and no LDS; each query row's
+// running max and sum are shared by its four lane groups through two
+// shuffles.  Long contexts are split over workgroups (flash-decoding style)
+// and the partial (max, sum, output) triples are merged in a second kernel in
+// split order.  Probabilities enter the second product rounded to bf16 and
+// the softmax sum is taken over the same rounded values, so every output row
+// is a convex combination of the visible value rows.
+#include <math.h>
+
+#include "common.hpp"
+#include "host.hpp"
+#include "kernels.hpp"
+#include "spec_verify.h"
+#include "spec_verify_attn.h"
+
+namespace sv {
+namespace {
+
+constexpr int kBlk = SV_KV_BLOCK;
+constexpr int kWavesPerGroup = 4;
+constexpr int kTargetUnits = 2048;    // waves the context split aims for (8 per CU)
+constexpr int kMinBlocksPerSplit = 4;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+struct AttnPlan {
+    int G = 0, nq = 0, nsplit = 1, bps = 0;
+    long long units = 0;
+    size_t ws_bytes = 0;
+};
+
+AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int Dh, int max_blocks) {
+    AttnPlan p;
+    p.G = Hq / Hkv;
+    p.nq = (p.G * T + 15) / 16;
+    const long long base = (long long)B * Hkv * p.nq;
+    long long ns = (kTargetUnits + base - 1) / base;
+    ns = ns < 1 ? 1 : ns;
+    const long long cap = max_blocks / kMinBlocksPerSplit > 0 ? max_blocks / kMinBlocksPerSplit : 1;
+    ns = ns > cap ? cap : ns;
+    p.bps = (int)((max_blocks + ns - 1) / ns);
+    p.nsplit = (max_blocks + p.bps - 1) / p.bps;
+    p.units = base * p.nsplit;
+    // partial output rows (16 per unit) and their (max, sum) pairs
+    p.ws_bytes = p.nsplit > 1 ? (size_t)p.units * 16 * (Dh + 2) * 4 : 0;
+    return p;
+}
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* kc;
+    const uint16_t* vc;
+    const int32_t* table;
+    const int32_t* ctx;
+    int B, T, Hq, Hkv, max_blocks, num_blocks, nq, nsplit, bps;
+    float scale_log2;     // softmax scale times log2(e): scores in the exp2 domain
+    float* part_o;        // [units*16, Dh] unnormalised partial outputs (split runs)
+    float* part_ml;       // [units*16, 2] partial (max, sum)
+    float* out;           // [B, T, Hq, Dh]
+};
+
+__device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
+
+template <int DH, bool kDirect>
+__global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_kernel(AttnArgs a) {
+    constexpr int KS = DH / 32;   // k steps of the score product
+    constexpr int DT = DH / 16;   // 16-dim tiles of the output
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const long long unit = (long long)blockIdx.x * kWavesPerGroup + wave;
+    const long long units = (long long)a.B * a.Hkv * a.nsplit * a.nq;
+    if (unit >= units) return;
+    const int qt = (int)(unit % a.nq);
+    long long rest = unit / a.nq;
+    const int sp = (int)(rest % a.nsplit);
+    rest /= a.nsplit;
+    const int kvh = (int)(rest % a.Hkv);
+    const int b = (int)(rest / a.Hkv);
+    const int G = a.Hq / a.Hkv;
+    const int c = lane & 15, g = lane >> 4;
+
+    // this lane's query row: position t, head h (column of S^T)
+    const int r = qt * 16 + c;
+    const bool row_ok = r < G * a.T;
+    const int t = row_ok ? r / G : 0;
+    const int h = kvh * G + r % G;
+    const int cap = a.max_blocks * kBlk;
+    const int ctx = clamp_ctx(a.ctx[b], cap);
+    const int vis = row_ok ? min(ctx + t + 1, cap) : 0;      // visible positions of the row
+    const int n_all = min(ctx + a.T, cap);                    // positions any row may see
+    const int kb0 = sp * a.bps;
+    const int kb1 = min((n_all + kBlk - 1) / kBlk, kb0 + a.bps);
+
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    bf16x8 qv[KS];
+    const uint16_t* qrow = a.q + (((size_t)b * a.T + t) * a.Hq + (h < a.Hq ? h : 0)) * DH;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        qv[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : zero8;
+
+    float m = -INFINITY, l = 0.f;
+    f32x4v acc[DT];
+#pragma unroll
+    for (int u = 0; u < DT; ++u) acc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+    for (int kb = kb0; kb < kb1; ++kb) {
+        int blk = trow[kb];
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        const uint16_t* kbase = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlk * DH;
+        const uint16_t* vbase = a.vc + ((size_t)blk * a.Hkv + kvh) * DH * kBlk;
+        // keys and values of the block, all loads in flight together
+        bf16x8 k0[KS], k1[KS], va[DT];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            k0[s] = *reinterpret_cast<const bf16x8*>(kbase + c * DH + 32 * s + 8 * g);
+            k1[s] = *reinterpret_cast<const bf16x8*>(kbase + (16 + c) * DH + 32 * s + 8 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+            const uint16_t* vrow = vbase + (16 * u + c) * kBlk;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
+            va[u] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
+        f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[s], qv[s], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qv[s], s1, 0, 0, 0);
+        }
+        // lane holds S^T[key 4g+i][row] in s0[i] and S^T[key 16+4g+i][row] in s1[i]
+        const int p0 = kb * kBlk + 4 * g;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = p0 + i < vis ? s0[i] * a.scale_log2 : -INFINITY;
+            x[4 + i] = p0 + 16 + i < vis ? s1[i] * a.scale_log2 : -INFINITY;
+        }
+        float bm = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+        const float mn = fmaxf(m, bm);
+        const float mref = mn == -INFINITY ? 0.f : mn;        // no visible key yet: p = 0
+        const float alpha = __builtin_amdgcn_exp2f(m - mref); // m = -inf: 0 (acc, l are 0)
+        uint32_t pb[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pb[i] = f32_to_bf16(__builtin_amdgcn_exp2f(x[i] - mref));
+            ps += __uint_as_float(pb[i] << 16);
+        }
+        ps += __shfl_xor(ps, 16, kWave);
+        ps += __shfl_xor(ps, 32, kWave);
+        l = l * alpha + ps;
+        m = mn;
+        const bf16x8 pv = __builtin_bit_cast(
+            bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                          pb[6] | (pb[7] << 16)});
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+            acc[u] *= alpha;
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], pv, acc[u], 0, 0, 0);
+        }
+    }
+
+    // lane holds O^T[dim 16u+4g+i][row] in acc[u][i]
+    if constexpr (kDirect) {
+        if (!row_ok) return;
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        float* orow = a.out + (((size_t)b * a.T + t) * a.Hq + h) * DH;
+#pragma unroll
+        for (int u = 0; u < DT; ++u)
+            *reinterpret_cast<f32x4v*>(orow + 16 * u + 4 * g) = acc[u] * inv;
+    } else {
+        const size_t prow = (size_t)unit * 16 + c;
+        float* orow = a.part_o + prow * DH;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4v*>(orow + 16 * u + 4 * g) = acc[u];
+        if (g == 0) {
+            a.part_ml[2 * prow] = m;
+            a.part_ml[2 * prow + 1] = l;
+        }
+    }
+}
+
+// Merge the context splits of every query row, in split order:
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;   // (row unit group, row, dim/4)
+    const int d4 = (int)(idx % (DH / 4));
+    long long rest = idx / (DH / 4);
+    const int c = (int)(rest % 16);
+    rest /= 16;
+    const int qt = (int)(rest % a.nq);
+    const long long bk = rest / a.nq;                                    // b * Hkv + kvh
+    if (bk >= (long long)a.B * a.Hkv) return;
+    const int G = a.Hq / a.Hkv;
+    const int r = qt * 16 + c;
+    if (r >= G * a.T) return;
+    const int kvh = (int)(bk % a.Hkv), b = (int)(bk / a.Hkv);
+    const int t = r / G, h = kvh * G + r % G;
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const size_t prow = ((size_t)(bk * a.nsplit + s) * a.nq + qt) * 16 + c;
+        M = fmaxf(M, a.part_ml[2 * prow]);
+    }
+    f32x4v o = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < a.nsplit; ++s) {
+            const size_t prow = ((size_t)(bk * a.nsplit + s) * a.nq + qt) * 16 + c;
+            const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * prow] - M);
+            L += w * a.part_ml[2 * prow + 1];
+            o += w * *reinterpret_cast<const f32x4v*>(a.part_o + prow * DH + 4 * d4);
+        }
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    *reinterpret_cast<f32x4v*>(a.out + (((size_t)b * a.T + t) * a.Hq + h) * DH + 4 * d4) = o * inv;
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ ctx_len, int B, int T, int Hkv, int max_blocks, int num_blocks) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;    // (b, t, kvh, dim)
+    const long long total = (long long)B * T * Hkv * DH;
+    if (idx >= total) return;
+    const int d = (int)(idx % DH);
+    long long rest = idx / DH;
+    const int kvh = (int)(rest % Hkv);
+    rest /= Hkv;
+    const int t = (int)(rest % T);
+    const int b = (int)(rest / T);
+    const int cap = max_blocks * kBlk;
+    const int p = clamp_ctx(ctx_len[b], cap) + t;
+    if (p >= cap) return;
+    int blk = table[(size_t)b * max_blocks + p / kBlk];
+    blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+    const int slot = p % kBlk;
+    kc[(((size_t)blk * Hkv + kvh) * kBlk + slot) * DH + d] = k_new[idx];
+    vc[(((size_t)blk * Hkv + kvh) * DH + d) * kBlk + slot] = v_new[idx];
+}
+
+__global__ void kv_commit_kernel(int32_t* ctx_len, const int32_t* accept_len, int B) {
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b < B && accept_len[b] >= 1) ctx_len[b] += accept_len[b];
+}
+
+int check_shapes(int B, int T, int Hq, int Hkv, int Dh, int max_blocks, int num_blocks) {
+    if (B < 0 || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv)
+        return fail(SV_ERR_INVALID_ARG, "attention: need B >= 0, T >= 1, Hq a multiple of Hkv >= 1");
+    if (Dh != 64 && Dh != 128) return fail(SV_ERR_UNSUPPORTED, "attention: head_dim must be 64 or 128");
+    if (max_blocks < 1 || num_blocks < 1)
+        return fail(SV_ERR_INVALID_ARG, "attention: max_blocks and num_blocks must be >= 1");
+    if ((long long)max_blocks * kBlk > (1 << 30))
+        return fail(SV_ERR_INVALID_ARG, "attention: max_blocks too large");
+    return SV_OK;
+}
+
+int launch_fail(hipError_t e, const char* what) {
+    return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+size_t spec_verify_attention_workspace_bytes(int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                                             int32_t head_dim, int32_t max_blocks) {
+    if (check_shapes(B, T, Hq, Hkv, head_dim, max_blocks, 1) != SV_OK || B == 0) return 0;
+    const size_t bytes = plan_attention(B, T, Hq, Hkv, head_dim, max_blocks).ws_bytes;
+    return bytes ? (bytes + 255) / 256 * 256 : 0;
+}
+
+int spec_verify_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          const int32_t* block_table, const int32_t* ctx_len, int32_t B, int32_t T,
+                          int32_t Hkv, int32_t head_dim, int32_t max_blocks, int32_t num_blocks,
+                          hipStream_t stream) {
+    int rc = check_shapes(B, T, Hkv, Hkv, head_dim, max_blocks, num_blocks);
+    if (rc != SV_OK) return rc;
+    if (B == 0) return SV_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !ctx_len)
+        return fail(SV_ERR_INVALID_ARG, "kv_append: null pointer");
+    const long long total = (long long)B * T * Hkv * head_dim;
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    ProfScope prof("kv_append", stream, 2.0 * total * 2 * 2, 0.0);
+    const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(v_new);
+    uint16_t* kc = static_cast<uint16_t*>(k_cache);
+    uint16_t* vc = static_cast<uint16_t*>(v_cache);
+    if (head_dim == 128)
+        SV_LAUNCH(prof, kv_append_kernel<128>, grid, 256, stream, kn, vn, kc, vc, block_table,
+                  ctx_len, B, T, Hkv, max_blocks, num_blocks);
+    else
+        SV_LAUNCH(prof, kv_append_kernel<64>, grid, 256, stream, kn, vn, kc, vc, block_table,
+                  ctx_len, B, T, Hkv, max_blocks, num_blocks);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : launch_fail(e, "kv_append launch");
+}
+
+int spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* ctx_len, int32_t B, int32_t T,
+                          int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t max_blocks,
+                          int32_t num_blocks, float scale, float* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    int rc = check_shapes(B, T, Hq, Hkv, head_dim, max_blocks, num_blocks);
+    if (rc != SV_OK) return rc;
+    if (B == 0) return SV_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !ctx_len || !out)
+        return fail(SV_ERR_INVALID_ARG, "attention: null pointer");
+    if (!isfinite(scale)) return fail(SV_ERR_INVALID_ARG, "attention: scale must be finite");
+    const AttnPlan p = plan_attention(B, T, Hq, Hkv, head_dim, max_blocks);
+    if (p.ws_bytes && (!ws || ws_bytes < p.ws_bytes))
+        return fail(SV_ERR_WORKSPACE, "attention: workspace of %zu bytes needed, %zu given",
+                    p.ws_bytes, ws_bytes);
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.kc = static_cast<const uint16_t*>(k_cache);
+    a.vc = static_cast<const uint16_t*>(v_cache);
+    a.table = block_table;
+    a.ctx = ctx_len;
+    a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv;
+    a.max_blocks = max_blocks; a.num_blocks = num_blocks;
+    a.nq = p.nq; a.nsplit = p.nsplit; a.bps = p.bps;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = out;
+    if (p.nsplit > 1) {
+        a.part_o = static_cast<float*>(ws);
+        a.part_ml = a.part_o + (size_t)p.units * 16 * head_dim;
+    }
+    const unsigned grid = (unsigned)((p.units + kWavesPerGroup - 1) / kWavesPerGroup);
+    // algorithmic bytes: every visible key and value once per (request, KV head) at the
+    // table's capacity, queries and outputs once
+    const double kv_bytes = (double)B * Hkv * max_blocks * kBlk * head_dim * 2 * 2;
+    const double flops = 4.0 * B * Hq * T * (double)max_blocks * kBlk * head_dim;
+    {
+        ProfScope prof("attention", stream, kv_bytes + (double)B * T * Hq * head_dim * 6, flops);
+#define SV_ATTN(DH, DIRECT)                                                                 \
+        SV_LAUNCH(prof, (attn_kernel<DH, DIRECT>), grid, kWavesPerGroup * kWave, stream, a)
+        if (head_dim == 128) {
+            if (p.nsplit > 1) SV_ATTN(128, false); else SV_ATTN(128, true);
+        } else {
+            if (p.nsplit > 1) SV_ATTN(64, false); else SV_ATTN(64, true);
+        }
+#undef SV_ATTN
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return launch_fail(e, "attention launch");
+    if (p.nsplit > 1) {
+        const long long threads = (long long)B * Hkv * p.nq * 16 * (head_dim / 4);
+        const unsigned cgrid = (unsigned)((threads + 255) / 256);
+        ProfScope prof("attention_combine", stream,
+                       (double)p.units * 16 * (head_dim + 2) * 4 + (double)B * T * Hq * head_dim * 4,
+                       0.0);
+        if (head_dim == 128)
+            SV_LAUNCH(prof, attn_combine_kernel<128>, cgrid, 256, stream, a);
+        else
+            SV_LAUNCH(prof, attn_combine_kernel<64>, cgrid, 256, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return launch_fail(e, "attention combine launch");
+    }
+    return SV_OK;
+}
+
+int spec_verify_kv_commit(int32_t* ctx_len, const int32_t* accept_len, int32_t B,
+                          hipStream_t stream) {
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "kv_commit: B < 0");
+    if (B == 0) return SV_OK;
+    if (!ctx_len || !accept_len) return fail(SV_ERR_INVALID_ARG, "kv_commit: null pointer");
+    ProfScope prof("kv_commit", stream, (double)B * 12, 0.0);
+    SV_LAUNCH(prof, kv_commit_kernel, (B + 255) / 256, 256, stream, ctx_len, accept_len, B);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : launch_fail(e, "kv_commit launch");
+}
+
+}  // extern "C"

@@ -32,6 +32,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "SWEEP_B", "SWEEP_K", "SWEEP_SIGMA",
     "make_model", "make_hidden", "make_synthetic_logits", "make_random_tokens",
+    "KV_BLOCK", "make_paged_attention", "ATTN_WORKLOADS",
     "bf16_bits_to_f32", "f32_to_bf16_bits",
 ]
 
@@ -84,7 +85,7 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # Stream ids keep every tensor's draws independent of every other tensor's.
 _STREAM = {"w_up": 1, "w_down": 2, "w_head": 3, "e_head": 4, "hidden": 5,
-           "logits_t": 6, "logits_noise": 7, "tokens": 8}
+           "logits_t": 6, "logits_noise": 7, "tokens": 8, "kv": 9, "kv_table": 10}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -190,3 +191,59 @@ def make_random_tokens(B: int, K: int, V: int, seed: int = 0, sub: int = 0) -> n
     """Uniform token ids [B, K] int32 (used where any valid draft will do)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _STREAM["tokens"], sub])))
     return g.integers(0, V, size=(B, K), dtype=np.int32)
+
+
+# ---- paged KV cache for the attention of the verified positions -------------
+KV_BLOCK = 32   # tokens per cache block
+
+# Attention shapes of the targets above (grouped-query heads, head dim 128):
+# Llama-8B-shaped 32 query / 8 KV heads, 70B-shaped 64 / 8, at the context
+# lengths the co-design post measures attention at (32K and 128K are the
+# post's; 4K and 8K are common serving contexts).
+ATTN_WORKLOADS = {
+    "8b-attn-b8-ctx8k": dict(B=8, Hq=32, Hkv=8, Dh=128, ctx=8192),
+    "70b-attn-b8-ctx8k": dict(B=8, Hq=64, Hkv=8, Dh=128, ctx=8192),
+    "8b-attn-b1-ctx32k": dict(B=1, Hq=32, Hkv=8, Dh=128, ctx=32768),
+    "70b-attn-b4-ctx32k": dict(B=4, Hq=64, Hkv=8, Dh=128, ctx=32768),
+    "8b-attn-b64-ctx4k": dict(B=64, Hq=32, Hkv=8, Dh=128, ctx=4096),
+}
+
+
+def make_paged_attention(B: int, T: int, Hq: int, Hkv: int, Dh: int, ctx, max_blocks: int,
+                         spare_blocks: int = 3, seed: int = 0, sub: int = 0) -> dict:
+    """A paged KV cache holding ctx[b] + T positions per request, in
+    physically shuffled blocks, plus the step's queries and new keys/values.
+
+    bf16 bit patterns (uint16) for q [B, T, Hq, Dh], k_new / v_new
+    [B, T, Hkv, Dh], k_cache [nb, Hkv, KV_BLOCK, Dh], v_cache [nb, Hkv, Dh,
+    KV_BLOCK]; block_table [B, max_blocks] int32 (unused entries 0), ctx_len
+    [B] int32.  Values N(0, 1); the first ctx[b] positions are filled, the
+    rest of the cache is left at zero for the step's append."""
+    ctx = np.asarray(ctx, dtype=np.int32)
+    need = [-(-(int(c) + T) // KV_BLOCK) for c in ctx]
+    assert max(need) <= max_blocks, "max_blocks too small for ctx + T"
+    nb = sum(need) + spare_blocks
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _STREAM["kv_table"], sub])))
+    ids = g.permutation(nb).astype(np.int32)
+    table = np.zeros((B, max_blocks), np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :need[b]] = ids[o:o + need[b]]
+        o += need[b]
+
+    def bf16(shape, stream_sub):
+        return f32_to_bf16_bits(_normal(shape, 1.0, seed, _STREAM["kv"], sub * 16 + stream_sub))
+
+    kc = np.zeros((nb, Hkv, KV_BLOCK, Dh), np.uint16)
+    vc = np.zeros((nb, Hkv, Dh, KV_BLOCK), np.uint16)
+    kfill, vfill = bf16((int(ctx.sum()) or 1, Hkv, Dh), 0), bf16((int(ctx.sum()) or 1, Hkv, Dh), 1)
+    o = 0
+    for b in range(B):
+        for p in range(int(ctx[b])):
+            blk, slot = table[b, p // KV_BLOCK], p % KV_BLOCK
+            kc[blk, :, slot, :] = kfill[o]
+            vc[blk, :, :, slot] = vfill[o]
+            o += 1
+    return {"q": bf16((B, T, Hq, Dh), 2), "k_new": bf16((B, T, Hkv, Dh), 3),
+            "v_new": bf16((B, T, Hkv, Dh), 4), "k_cache": kc, "v_cache": vc,
+            "block_table": table, "ctx_len": ctx.copy(), "num_blocks": nb}

@@ -443,6 +443,71 @@ def _k_table(a):
         print(json.dumps(res), flush=True)
 
 
+ATTN_K = (0, 1, 3, 7, 15)
+
+
+def _attention_bench(a):
+    """Paged attention of the T = K + 1 verified positions over a full KV
+    cache: time per call (eager, back to back), the KV bytes it must read
+    once, and the fraction of HBM bandwidth; the attention GEMM-M per KV head
+    is G (K + 1) (NVIDIA co-design post, 'Draft length and attention
+    performance').  Cache contents are seeded random bf16 drawn on the GPU."""
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    for name, c in workload.ATTN_WORKLOADS.items():
+        B, Hq, Hkv, Dh, ctx = c["B"], c["Hq"], c["Hkv"], c["Dh"], c["ctx"]
+        G = Hq // Hkv
+        for K in ATTN_K:
+            T = K + 1
+            mb = -(-(ctx + T) // workload.KV_BLOCK)
+            nb = B * mb
+            gen = torch.Generator(device="cuda").manual_seed(1234)
+            kc = torch.randn((nb, Hkv, workload.KV_BLOCK, Dh), generator=gen, device="cuda").to(torch.bfloat16)
+            vc = torch.randn((nb, Hkv, Dh, workload.KV_BLOCK), generator=gen, device="cuda").to(torch.bfloat16)
+            perm = torch.randperm(nb, generator=gen, device="cuda").to(torch.int32)
+            table = perm.view(B, mb).contiguous()
+            ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+            q = torch.randn((B, T, Hq, Dh), generator=gen, device="cuda").to(torch.bfloat16)
+            kn = torch.randn((B, T, Hkv, Dh), generator=gen, device="cuda").to(torch.bfloat16)
+            vn = torch.randn((B, T, Hkv, Dh), generator=gen, device="cuda").to(torch.bfloat16)
+            out = torch.empty((B, T, Hq, Dh), dtype=torch.float32, device="cuda")
+            n = sv.attention_workspace_bytes(B, T, Hq, Hkv, Dh, mb)
+            ws = sv.workspace(n) if n else None
+            sv.kv_append(kn, vn, kc, vc, table, ctx_len)
+            scale = 1.0 / math.sqrt(Dh)
+            ms = _time_fn(lambda s: sv.attention(q, kc, vc, table, ctx_len, scale, out=out, ws=ws,
+                                                 stream=s), 50, 5, a.graph)
+            sv.profile_begin(1 << 12)
+            for _ in range(5):
+                sv.attention(q, kc, vc, table, ctx_len, scale, out=out, ws=ws)
+                sv.kv_append(kn, vn, kc, vc, table, ctx_len)
+            torch.cuda.synchronize()
+            kt = sv.profile_end(16)
+            kv_bytes = B * Hkv * (ctx + T) * Dh * 2 * 2
+            io_bytes = B * T * Hq * Dh * (2 + 4)
+            flops = 4.0 * B * Hq * T * (ctx + (T + 1) / 2.0) * Dh
+            main = kt.get("attention", (5, 5 * ms, 0, 0))
+            comb = kt.get("attention_combine", (0, 0.0, 0, 0))
+            app = kt.get("kv_append", (5, 0.0, 0, 0))
+            comb_us = comb[1] / comb[0] * 1e3 if comb[0] else 0.0
+            attn_us = main[1] / main[0] * 1e3 + comb_us    # both launches of one call
+            res = {"attention": name, "B": B, "Hq": Hq, "Hkv": Hkv, "G": G, "Dh": Dh, "ctx": ctx,
+                   "K": K, "T": T, "gemm_m_per_kv_head": G * T,
+                   "launch": "hipgraph" if a.graph else "eager",
+                   "us_per_call": ms * 1e3,
+                   "kernel_us": attn_us,
+                   "combine_us": comb_us,
+                   "append_us": app[1] / app[0] * 1e3 if app[0] else 0.0,
+                   "kv_bytes": kv_bytes,
+                   "achieved_GBps": (kv_bytes + io_bytes) / (attn_us * 1e-6) / 1e9,
+                   "hbm_frac": (kv_bytes + io_bytes) / (attn_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+                   "TFLOPs": flops / (attn_us * 1e-6) / 1e12,
+                   "verified_positions_per_s": B * T / (ms / 1e3)}
+            print(json.dumps(res), flush=True)
+            del kc, vc, q, kn, vn, out, ws, table, perm, ctx_len
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +525,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--attention", action="store_true",
+                    help="paged attention of the verified positions: time and HBM roofline per "
+                         "workload and draft length")
     ap.add_argument("--k-table", action="store_true",
                     help="measure T_verif(M) and AL(K) on the sweep stack and print the "
                          "goodput-optimal draft length per batch size")
@@ -490,6 +558,9 @@ def main():
         return
     if a.k_table:
         _k_table(a)
+        return
+    if a.attention:
+        _attention_bench(a)
         return
     if a.crossover:
         # forward-only time per row count with each MFMA family forced: the

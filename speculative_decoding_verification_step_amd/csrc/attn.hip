@@ -18,11 +18,14 @@
 // 0, then keys 16+4g..16+4g+3 of tile 1) - the A operand V^T uses the same
 // order - so the softmax needs no transpose and no LDS; each query row's
 // running max and sum are shared by its four lane groups through two
-// shuffles.  Long contexts are split over workgroups (flash-decoding style)
-// and the partial (max, sum, output) triples are merged in a second kernel in
-// split order.  Probabilities enter the second product rounded to bf16 and
-// the softmax sum is taken over the same rounded values, so every output row
-// is a convex combination of the visible value rows.
+// shuffles.  The four waves of a workgroup take interleaved blocks of one
+// context range (each prefetching its next block into a second register
+// set) and merge their (max, sum, output) states through LDS; long contexts
+// are further split over workgroups (flash-decoding style) and the partial
+// states are merged in a second kernel in split order.  Probabilities enter
+// the second product rounded to bf16 and the softmax sum is taken over the
+// same rounded values, so every output row is a convex combination of the
+// visible value rows.
 #include <math.h>
 
 #include "common.hpp"
@@ -36,8 +39,8 @@ namespace {
 
 constexpr int kBlk = SV_KV_BLOCK;
 constexpr int kWavesPerGroup = 4;
-constexpr int kTargetUnits = 2048;    // waves the context split aims for (8 per CU)
-constexpr int kMinBlocksPerSplit = 4;
+constexpr int kTargetUnits = 512;     // workgroups the context split aims for (2 per CU)
+constexpr int kMinBlocksPerSplit = 8; // two blocks per wave at least
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -79,15 +82,23 @@ struct AttnArgs {
 
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
+template <int DH>
+struct KVRegs {
+    bf16x8 k0[DH / 32], k1[DH / 32], v[DH / 16];
+};
+
 template <int DH, bool kDirect>
-__global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void attn_kernel(AttnArgs a) {
     constexpr int KS = DH / 32;   // k steps of the score product
     constexpr int DT = DH / 16;   // 16-dim tiles of the output
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const long long unit = (long long)blockIdx.x * kWavesPerGroup + wave;
-    const long long units = (long long)a.B * a.Hkv * a.nsplit * a.nq;
-    if (unit >= units) return;
+    // XCD-contiguous renumbering (workgroup i runs on XCD i % 8): the query
+    // tiles of one (request, KV head, range) get consecutive numbers on one
+    // XCD and read its blocks through one L2
+    const int wg = blockIdx.x, Gn = gridDim.x;
+    const int q8 = Gn / 8, r8 = Gn % 8, x8 = wg % 8, j8 = wg / 8;
+    const long long unit = x8 < r8 ? x8 * (q8 + 1) + j8 : r8 * (q8 + 1) + (x8 - r8) * q8 + j8;
     const int qt = (int)(unit % a.nq);
     long long rest = unit / a.nq;
     const int sp = (int)(rest % a.nsplit);
@@ -106,8 +117,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_kernel(AttnArgs a
     const int ctx = clamp_ctx(a.ctx[b], cap);
     const int vis = row_ok ? min(ctx + t + 1, cap) : 0;      // visible positions of the row
     const int n_all = min(ctx + a.T, cap);                    // positions any row may see
-    const int kb0 = sp * a.bps;
-    const int kb1 = min((n_all + kBlk - 1) / kBlk, kb0 + a.bps);
+    const int kb_end = min((n_all + kBlk - 1) / kBlk, (sp + 1) * a.bps);
 
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     bf16x8 qv[KS];
@@ -122,30 +132,30 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_kernel(AttnArgs a
     for (int u = 0; u < DT; ++u) acc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
     const int32_t* trow = a.table + (size_t)b * a.max_blocks;
-    for (int kb = kb0; kb < kb1; ++kb) {
+    auto load = [&](KVRegs<DH>& kv, int kb) {
         int blk = trow[kb];
         blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
         const uint16_t* kbase = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlk * DH;
         const uint16_t* vbase = a.vc + ((size_t)blk * a.Hkv + kvh) * DH * kBlk;
-        // keys and values of the block, all loads in flight together
-        bf16x8 k0[KS], k1[KS], va[DT];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            k0[s] = *reinterpret_cast<const bf16x8*>(kbase + c * DH + 32 * s + 8 * g);
-            k1[s] = *reinterpret_cast<const bf16x8*>(kbase + (16 + c) * DH + 32 * s + 8 * g);
+            kv.k0[s] = *reinterpret_cast<const bf16x8*>(kbase + c * DH + 32 * s + 8 * g);
+            kv.k1[s] = *reinterpret_cast<const bf16x8*>(kbase + (16 + c) * DH + 32 * s + 8 * g);
         }
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
             const uint16_t* vrow = vbase + (16 * u + c) * kBlk;
             const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
             const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-            va[u] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+            kv.v[u] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         }
+    };
+    auto process = [&](const KVRegs<DH>& kv, int kb) {
         f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[s], qv[s], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qv[s], s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k0[s], qv[s], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k1[s], qv[s], s1, 0, 0, 0);
         }
         // lane holds S^T[key 4g+i][row] in s0[i] and S^T[key 16+4g+i][row] in s1[i]
         const int p0 = kb * kBlk + 4 * g;
@@ -180,26 +190,63 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_kernel(AttnArgs a
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
             acc[u] *= alpha;
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], pv, acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.v[u], pv, acc[u], 0, 0, 0);
         }
+    };
+
+    // this wave's blocks: kb0 + wave, + 4, + 8, ... (next one prefetched)
+    KVRegs<DH> bufa, bufb;
+    int kb = sp * a.bps + wave;
+    if (kb < kb_end) load(bufa, kb);
+    for (; kb < kb_end; kb += 2 * kWavesPerGroup) {
+        if (kb + kWavesPerGroup < kb_end) load(bufb, kb + kWavesPerGroup);
+        process(bufa, kb);
+        if (kb + kWavesPerGroup >= kb_end) break;
+        if (kb + 2 * kWavesPerGroup < kb_end) load(bufa, kb + 2 * kWavesPerGroup);
+        process(bufb, kb + kWavesPerGroup);
     }
 
-    // lane holds O^T[dim 16u+4g+i][row] in acc[u][i]
-    if constexpr (kDirect) {
-        if (!row_ok) return;
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        float* orow = a.out + (((size_t)b * a.T + t) * a.Hq + h) * DH;
+    // merge the four waves' states (fixed wave order); lane holds O^T[dim
+    // 16u+4g+i][row] in acc[u][i], and (m, l) of its row
+    __shared__ float sm[kWavesPerGroup][16], sl[kWavesPerGroup][16];
+    __shared__ f32x4v so[kWavesPerGroup][DT][kWave];
+    if (g == 0) {
+        sm[wave][c] = m;
+        sl[wave][c] = l;
+    }
 #pragma unroll
-        for (int u = 0; u < DT; ++u)
-            *reinterpret_cast<f32x4v*>(orow + 16 * u + 4 * g) = acc[u] * inv;
-    } else {
-        const size_t prow = (size_t)unit * 16 + c;
-        float* orow = a.part_o + prow * DH;
+    for (int u = 0; u < DT; ++u) so[wave][u][lane] = acc[u];
+    __syncthreads();
+    float M = sm[0][c];
 #pragma unroll
-        for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4v*>(orow + 16 * u + 4 * g) = acc[u];
-        if (g == 0) {
-            a.part_ml[2 * prow] = m;
-            a.part_ml[2 * prow + 1] = l;
+    for (int w = 1; w < kWavesPerGroup; ++w) M = fmaxf(M, sm[w][c]);
+    float e[kWavesPerGroup], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+        e[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][c] - M);
+        L += e[w] * sl[w][c];
+    }
+    // wave w finishes the output tiles u = w, w + 4, ...
+    const size_t prow = (size_t)unit * 16 + c;
+#pragma unroll
+    for (int u = wave; u < DT; u += kWavesPerGroup) {
+        f32x4v o = e[0] * so[0][u][lane];
+#pragma unroll
+        for (int w = 1; w < kWavesPerGroup; ++w) o += e[w] * so[w][u][lane];
+        if constexpr (kDirect) {
+            if (row_ok) {
+                const float inv = L > 0.f ? 1.0f / L : 0.f;
+                *reinterpret_cast<f32x4v*>(a.out + (((size_t)b * a.T + t) * a.Hq + h) * DH +
+                                           16 * u + 4 * g) = o * inv;
+            }
+        } else {
+            *reinterpret_cast<f32x4v*>(a.part_o + prow * DH + 16 * u + 4 * g) = o;
+        }
+    }
+    if constexpr (!kDirect) {
+        if (wave == 0 && g == 0) {
+            a.part_ml[2 * prow] = M;
+            a.part_ml[2 * prow + 1] = L;
         }
     }
 }
@@ -222,6 +269,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int kvh = (int)(bk % a.Hkv), b = (int)(bk / a.Hkv);
     const int t = r / G, h = kvh * G + r % G;
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < a.nsplit; ++s) {
         const size_t prow = ((size_t)(bk * a.nsplit + s) * a.nq + qt) * 16 + c;
         M = fmaxf(M, a.part_ml[2 * prow]);
@@ -229,6 +277,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     f32x4v o = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != -INFINITY) {
+#pragma unroll 8
         for (int s = 0; s < a.nsplit; ++s) {
             const size_t prow = ((size_t)(bk * a.nsplit + s) * a.nq + qt) * 16 + c;
             const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * prow] - M);
@@ -354,7 +403,7 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
         a.part_o = static_cast<float*>(ws);
         a.part_ml = a.part_o + (size_t)p.units * 16 * head_dim;
     }
-    const unsigned grid = (unsigned)((p.units + kWavesPerGroup - 1) / kWavesPerGroup);
+    const unsigned grid = (unsigned)p.units;
     // algorithmic bytes: every visible key and value once per (request, KV head) at the
     // table's capacity, queries and outputs once
     const double kv_bytes = (double)B * Hkv * max_blocks * kBlk * head_dim * 2 * 2;

@@ -41,6 +41,7 @@ constexpr int kBlk = SV_KV_BLOCK;
 constexpr int kWavesPerGroup = 4;
 constexpr int kTargetUnits = 512;     // workgroups the context split aims for (2 per CU)
 constexpr int kMinBlocksPerSplit = 8; // two blocks per wave at least
+constexpr float kLazyMargin = 8.0f;   // log2 units a score may exceed the running max by
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void attn_kernel(AttnArg
     for (int s = 0; s < KS; ++s)
         qv[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : zero8;
 
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, lpart = 0.f;
     f32x4v acc[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) acc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
@@ -165,46 +166,65 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void attn_kernel(AttnArg
             x[i] = p0 + i < vis ? s0[i] * a.scale_log2 : -INFINITY;
             x[4 + i] = p0 + 16 + i < vis ? s1[i] * a.scale_log2 : -INFINITY;
         }
-        float bm = x[0];
+        // Lazy running max: the reference m (equal in the row's four lane
+        // groups) moves only when some score exceeds it by more than
+        // kLazyMargin (log2 units), found with one wave-wide vote; the
+        // exact row max and the rescale then run.  Otherwise p <= 2^margin
+        // and no cross-lane exchange is needed; the sum stays per lane group.
+        float lm = x[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-        const float mn = fmaxf(m, bm);
-        const float mref = mn == -INFINITY ? 0.f : mn;        // no visible key yet: p = 0
-        const float alpha = __builtin_amdgcn_exp2f(m - mref); // m = -inf: 0 (acc, l are 0)
+        for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
+        if (__ballot(lm > m + kLazyMargin)) {
+            float bm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+            const float mn = fmaxf(m, bm);
+            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+            lpart *= alpha;
+#pragma unroll
+            for (int u = 0; u < DT; ++u) acc[u] *= alpha;
+            m = mn;
+        }
+        const float mref = m == -INFINITY ? 0.f : m;          // no visible key yet: p = 0
         uint32_t pb[8];
-        float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             pb[i] = f32_to_bf16(__builtin_amdgcn_exp2f(x[i] - mref));
-            ps += __uint_as_float(pb[i] << 16);
+            lpart += __uint_as_float(pb[i] << 16);
         }
-        ps += __shfl_xor(ps, 16, kWave);
-        ps += __shfl_xor(ps, 32, kWave);
-        l = l * alpha + ps;
-        m = mn;
         const bf16x8 pv = __builtin_bit_cast(
             bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
                           pb[6] | (pb[7] << 16)});
 #pragma unroll
-        for (int u = 0; u < DT; ++u) {
-            acc[u] *= alpha;
+        for (int u = 0; u < DT; ++u)
             acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.v[u], pv, acc[u], 0, 0, 0);
-        }
     };
 
-    // this wave's blocks: kb0 + wave, + 4, + 8, ... (next one prefetched)
+    // this wave's blocks: kb0 + wave, + 4, + 8, ..., the next one always in
+    // flight.  The wave index is made provably uniform, so block ids come
+    // through scalar loads, and the loop body has no branch around its loads:
+    // the wait before a block's products then covers only the older block.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int first = sp * a.bps + wv;
+    const int nmine = first < kb_end ? (kb_end - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
+    const int last = first + kWavesPerGroup * (nmine - 1);
     KVRegs<DH> bufa, bufb;
-    int kb = sp * a.bps + wave;
-    if (kb < kb_end) load(bufa, kb);
-    for (; kb < kb_end; kb += 2 * kWavesPerGroup) {
-        if (kb + kWavesPerGroup < kb_end) load(bufb, kb + kWavesPerGroup);
-        process(bufa, kb);
-        if (kb + kWavesPerGroup >= kb_end) break;
-        if (kb + 2 * kWavesPerGroup < kb_end) load(bufa, kb + 2 * kWavesPerGroup);
-        process(bufb, kb + kWavesPerGroup);
+    if (nmine > 0) {
+        int kb = first;
+        load(bufa, kb);
+        for (int i = 0;; i += 2) {
+            load(bufb, min(kb + kWavesPerGroup, last));
+            process(bufa, kb);
+            if (i + 1 >= nmine) break;
+            load(bufa, min(kb + 2 * kWavesPerGroup, last));
+            process(bufb, kb + kWavesPerGroup);
+            if (i + 2 >= nmine) break;
+            kb += 2 * kWavesPerGroup;
+        }
     }
+
+    // the row's softmax sum over its four lane groups
+    float l = lpart + __shfl_xor(lpart, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
 
     // merge the four waves' states (fixed wave order); lane holds O^T[dim
     // 16u+4g+i][row] in acc[u][i], and (m, l) of its row

@@ -33,6 +33,7 @@ __all__ = [
     "Workload", "WORKLOADS", "SWEEP_B", "SWEEP_K", "SWEEP_SIGMA",
     "make_model", "make_hidden", "make_synthetic_logits", "make_random_tokens",
     "KV_BLOCK", "make_paged_attention", "ATTN_WORKLOADS",
+    "MoEWorkload", "MOE_WORKLOADS", "make_moe_model",
     "bf16_bits_to_f32", "f32_to_bf16_bits",
 ]
 
@@ -85,7 +86,8 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # Stream ids keep every tensor's draws independent of every other tensor's.
 _STREAM = {"w_up": 1, "w_down": 2, "w_head": 3, "e_head": 4, "hidden": 5,
-           "logits_t": 6, "logits_noise": 7, "tokens": 8, "kv": 9, "kv_table": 10}
+           "logits_t": 6, "logits_noise": 7, "tokens": 8, "kv": 9, "kv_table": 10,
+           "moe_router": 11, "moe_up": 12, "moe_down": 13}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -247,3 +249,67 @@ def make_paged_attention(B: int, T: int, Hq: int, Hkv: int, Dh: int, ctx, max_bl
     return {"q": bf16((B, T, Hq, Dh), 2), "k_new": bf16((B, T, Hkv, Dh), 3),
             "v_new": bf16((B, T, Hkv, Dh), 4), "k_cache": kc, "v_cache": vc,
             "block_table": table, "ctx_len": ctx.copy(), "num_blocks": nb}
+
+
+# ---- mixture-of-experts target ------------------------------------------------
+@dataclass(frozen=True)
+class MoEWorkload:
+    """A stack of pre-norm MoE blocks: a router [E, d] picks top_k of
+    n_experts SiLU MLP experts (up [ffn, d], down [d, ffn]) per position; a
+    final RMSNorm and the LM head follow.  bf16 weights, std 0.02."""
+    name: str
+    d: int
+    ffn: int             # per expert
+    n_experts: int
+    top_k: int
+    n_layers: int
+    vocab: int
+    B: int
+    K: int
+    sigma: float
+    temperature: float
+    seed: int = 0
+
+    @property
+    def M(self) -> int:
+        return self.B * (self.K + 1)
+
+    weight_std = 0.02
+
+    def expert_elems(self) -> int:
+        return 2 * self.d * self.ffn
+
+    def with_batch(self, B: int, K: int, **kw) -> "MoEWorkload":
+        return replace(self, B=B, K=K, **kw)
+
+
+# 64 fine-grained experts, 6 active per position: a small-expert MoE whose
+# expert weights (2.95 GB over 4 blocks) dominate, so the bytes a step streams
+# grow with the number of distinct experts its B*(K+1) positions touch.
+MOE_WORKLOADS = {
+    "moe-64e-top6-b1-k4": MoEWorkload("moe-64e-top6-b1-k4", 2048, 1408, 64, 6, 4, 32000, 1, 4,
+                                      0.3, 1.0),
+}
+
+
+def make_moe_model(w: MoEWorkload, sigma: float | None = None, draft_head: bool = True) -> dict:
+    """MoE weights as bf16 bit patterns: ``w_router`` [L, E, d], ``w_up``
+    [L, E, ffn, d], ``w_down`` [L, E, d, ffn], ``w_head`` [V, d] (and the
+    draft head ``w_head + sigma E``), ``gain`` [L+1, d] ones."""
+    sigma = w.sigma if sigma is None else sigma
+    std = w.weight_std
+    L, E, d, f, V = w.n_layers, w.n_experts, w.d, w.ffn, w.vocab
+    model = {
+        "w_router": _as_weight(_normal((L, E, d), std, w.seed, _STREAM["moe_router"]), "bf16"),
+        "w_up": _as_weight(_normal((L, E, f, d), std, w.seed, _STREAM["moe_up"]), "bf16"),
+        "w_down": _as_weight(_normal((L, E, d, f), std, w.seed, _STREAM["moe_down"]), "bf16"),
+        "gain": np.ones((L + 1, d), dtype=np.float32),
+    }
+    head32 = _normal((V, d), std, w.seed, _STREAM["w_head"])
+    model["w_head"] = _as_weight(head32, "bf16")
+    if draft_head:
+        e = _normal((V, d), std, w.seed, _STREAM["e_head"])
+        e *= np.float32(sigma)
+        e += bf16_bits_to_f32(model["w_head"])
+        model["w_draft_head"] = _as_weight(e, "bf16")
+    return model

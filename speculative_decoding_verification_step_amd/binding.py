@@ -76,6 +76,10 @@ EXPORTS = {
     "sv_kv_pool_reserve": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32]),
     "sv_kv_pool_trim": (ctypes.c_int, [_vp, _vp, _vp, _i32]),
     "spec_verify_window_k": (_i32, [_vp, _i32, _i32, ctypes.c_float, _i32, _i32]),
+    "sv_moe_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_vp)]),
+    "sv_moe_destroy": (None, [_vp]),
+    "spec_verify_moe_workspace_bytes": (_sz, [_vp, _i32]),
+    "spec_verify_moe_forward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -433,3 +437,63 @@ class KVPool:
         n = _i32(n_blocks)
         _check(lib().sv_kv_pool_trim(self._h, row.ctypes.data, ctypes.byref(n), tokens))
         return n.value
+
+
+# ---- mixture-of-experts target (include/spec_verify_moe.h) --------------------
+class MoEDesc(ctypes.Structure):
+    _fields_ = [("d", _i32), ("ffn", _i32), ("n_experts", _i32), ("top_k", _i32),
+                ("n_layers", _i32), ("vocab", _i32), ("rms_eps", ctypes.c_float),
+                ("w_router", _vp), ("w_up", _vp), ("w_down", _vp), ("gain", _vp), ("w_head", _vp)]
+
+
+class MoEModel:
+    """Borrowed view of packed MoE weights on the GPU (bf16, tiled).  Use
+    ``MoEModel.packed`` to pack row-major weights: w_router [L, E, d],
+    w_up [L, E, ffn, d], w_down [L, E, d, ffn], w_head [V, d], gain [L+1, d]."""
+
+    def __init__(self, w_router, w_up, w_down, gain, w_head, dims, top_k: int,
+                 rms_eps: float = 1e-5):
+        L, E, d, ffn, V = dims
+        _need(gain, "gain", torch.float32, (L + 1, d))
+        for t, name in ((w_router, "w_router"), (w_up, "w_up"), (w_down, "w_down"), (w_head, "w_head")):
+            _need(t, name, torch.bfloat16)
+        self._keep = (w_router, w_up, w_down, gain, w_head)
+        self.n_layers, self.n_experts, self.d, self.ffn, self.vocab = L, E, d, ffn, V
+        self.top_k = top_k
+        desc = MoEDesc(d, ffn, E, top_k, L, V, rms_eps, _ptr(w_router), _ptr(w_up), _ptr(w_down),
+                       _ptr(gain), _ptr(w_head))
+        h = _vp()
+        _check(lib().sv_moe_create(ctypes.addressof(desc), ctypes.byref(h)))
+        self._h = h
+
+    @classmethod
+    def packed(cls, w_router, w_up, w_down, gain, w_head, top_k: int, rms_eps: float = 1e-5):
+        L, E, d = w_router.shape
+        ffn = w_up.shape[2]
+        V = w_head.shape[0]
+        return cls(pack(w_router), pack(w_up.reshape(L * E, ffn, d)), pack(w_down.reshape(L * E, d, ffn)),
+                   gain, pack(w_head), (L, E, d, ffn, V), top_k, rms_eps)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.sv_moe_destroy(self._h)
+            self._h = None
+
+    def workspace_bytes(self, M: int) -> int:
+        return int(lib().spec_verify_moe_workspace_bytes(self._h, M))
+
+    def forward(self, hidden, logits=None, active=None, ws=None, stream=None):
+        """Logits [M, V] fp32; ``active`` (int32 [n_layers] on the GPU) gets the
+        distinct experts each block used."""
+        M = hidden.shape[0]
+        _need(hidden, "hidden", torch.float32, (M, self.d))
+        if logits is None:
+            logits = torch.empty((M, self.vocab), dtype=torch.float32, device=hidden.device)
+        _need(logits, "logits", torch.float32, (M, self.vocab))
+        if active is not None:
+            _need(active, "active", torch.int32, (self.n_layers,))
+        if ws is None:
+            ws = workspace(self.workspace_bytes(M), hidden.device)
+        _check(lib().spec_verify_moe_forward(self._h, _ptr(hidden), M, _ptr(logits), _ptr(active),
+                                             _ptr(ws), ws.numel(), _stream(stream)))
+        return logits

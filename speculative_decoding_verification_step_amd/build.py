@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = ["api.hip", "attn.hip", "gemm.hip", "kselect.cpp", "kvpool.cpp", "matmul.hip", "gemv.hip",
-           "mfma.hip", "norm.hip", "pack.hip", "vocab.hip"]
+           "mfma.hip", "moe.hip", "norm.hip", "pack.hip", "vocab.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

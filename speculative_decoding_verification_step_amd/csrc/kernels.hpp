@@ -30,7 +30,7 @@ struct MatmulArgs {
     int splits;           // kEpiResidual on the MFMA kernels: K split count (0 = add
                           // into h); `out` then holds `splits` fp32 partial
                           // planes [M, N] that the next RMSNorm folds in
-    const char* name;     // timing label, set by launch_matmul
+    const char* name;     // timing label (null: launch_matmul names it by kernel and epilogue)
 };
 
 // bf16 weights: elements of the MFMA-tiled copy of a [rows, cols] matrix

@@ -27,7 +27,7 @@ hipError_t launch_matmul(const MatmulArgs& a, int kind, hipStream_t stream) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (kind < 0 || kind > 2 || a.epi < 0 || a.epi > 2) return hipErrorInvalidValue;
     MatmulArgs b = a;
-    b.name = scope_name(kind, a.epi);
+    b.name = a.name ? a.name : scope_name(kind, a.epi);
     switch (kind) {
         case kGemvValu: return launch_gemv(b, stream);
         case kMfmaSkinny: return launch_mfma_skinny(b, stream);

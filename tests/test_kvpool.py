@@ -80,3 +80,27 @@ def test_attention_host_checks(lib):
     assert L.spec_verify_kv_commit(None, None, 0, None) == sv.SV_OK
     assert L.spec_verify_kv_commit(None, F, 3, None) == sv.SV_ERR_INVALID_ARG
     assert L.spec_verify_kv_append(F, F, F, F, F, F, 1, 1, 8, 80, 4, 4, None) == sv.SV_ERR_UNSUPPORTED
+
+
+def test_moe_host_checks(lib):
+    L = lib
+    d = sv.binding.MoEDesc(256, 128, 16, 4, 2, 100, 1e-5, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    import ctypes
+    h = ctypes.c_void_p()
+    assert L.sv_moe_create(ctypes.addressof(d), ctypes.byref(h)) == sv.SV_OK
+    try:
+        assert L.spec_verify_moe_workspace_bytes(h, 1025) == 0
+        assert L.spec_verify_moe_forward(h, 0x10000, 1025, 0x10000, None, 0x10000, 1 << 30, None) \
+            == sv.SV_ERR_UNSUPPORTED
+        assert L.spec_verify_moe_forward(h, 0x10000, 8, 0x10000, None, 0x10000, 16, None) \
+            == sv.SV_ERR_WORKSPACE
+        assert L.spec_verify_moe_forward(h, None, 0, None, None, None, 0, None) == sv.SV_OK
+    finally:
+        L.sv_moe_destroy(h)
+    for bad in (dict(top_k=9), dict(top_k=17), dict(d=100), dict(ffn=40), dict(n_experts=300)):
+        kw = dict(d=256, ffn=128, n_experts=16, top_k=4)
+        kw.update(bad)
+        dd = sv.binding.MoEDesc(kw["d"], kw["ffn"], kw["n_experts"], kw["top_k"], 2, 100, 1e-5,
+                                0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+        h2 = ctypes.c_void_p()
+        assert L.sv_moe_create(ctypes.addressof(dd), ctypes.byref(h2)) != sv.SV_OK

@@ -443,6 +443,97 @@ def _k_table(a):
         print(json.dumps(res), flush=True)
 
 
+MOE_B = (1, 2, 4, 8, 16, 32, 64)
+MOE_K = tuple(range(9))
+
+
+def _moe_bench(a):
+    """Verification step of the 64-expert top-6 MoE stack over B x K: the
+    forward (reporting the distinct experts each block touched, so the bytes
+    streamed are the experts actually used) plus rejection sampling; then the
+    library's goodput-optimal K per batch size from the measured times and
+    acceptance lengths (Cohere DSD: for MoE the optimum need not fall with B)."""
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    from oracle import moe as om
+    w = workload.MOE_WORKLOADS["moe-64e-top6-b1-k4"]
+    T = 1.0
+    for sigma in workload.SWEEP_SIGMA:
+        model = workload.make_moe_model(w, sigma=sigma)
+
+        def dev(x):
+            return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        L, E, d, f, V = w.n_layers, w.n_experts, w.d, w.ffn, w.vocab
+        pr, pu, pd = sv.pack(dev(model["w_router"])), sv.pack(dev(model["w_up"]).reshape(L * E, f, d)), \
+            sv.pack(dev(model["w_down"]).reshape(L * E, d, f))
+        gain = torch.from_numpy(model["gain"]).cuda()
+        target = sv.MoEModel(pr, pu, pd, gain, sv.pack(dev(model["w_head"])), (L, E, d, f, V), w.top_k)
+        drafter = sv.MoEModel(pr, pu, pd, gain, sv.pack(dev(model["w_draft_head"])), (L, E, d, f, V),
+                              w.top_k)
+        del model
+        times, al_by_k, points = {}, {0: 1.0}, []
+        expert_bytes = 2.0 * d * f * 2
+        for K in MOE_K:
+            for B in MOE_B:
+                M = B * (K + 1)
+                g = np.random.default_rng(1000 * B + K)
+                hidden = torch.from_numpy(g.standard_normal((M, d)).astype(np.float32)).cuda()
+                zq = drafter.forward(hidden).view(B, K + 1, V)[:, :K].contiguous()
+                x = _draft_tokens(zq, T, 7)
+                logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+                active = torch.zeros(L, dtype=torch.int32, device="cuda")
+                fws = sv.workspace(target.workspace_bytes(M))
+                aws = sv.workspace(sv.accept_workspace_bytes(B, K, V))
+                out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+                al = torch.empty((B,), dtype=torch.int32, device="cuda")
+
+                def step(s, stp=0):
+                    target.forward(hidden, logits, active=active, ws=fws, stream=s)
+                    sv.accept(logits.view(B, K + 1, V), zq if K else None, x if K else None, T, 0, stp,
+                              out_tokens=out, accept_len=al, ws=aws, stream=s)
+                ms = _time_fn(step, 20, 2, a.graph)
+                act = cpu_ints(active)
+                if K and B == MOE_B[-1]:
+                    als = []
+                    for stp in range(16):
+                        xs = _draft_tokens(zq, T, 3000 + stp)
+                        target.forward(hidden, logits, active=active, ws=fws)
+                        sv.accept(logits.view(B, K + 1, V), zq, xs, T, 0, stp, out_tokens=out,
+                                  accept_len=al, ws=aws)
+                        als.append(al.cpu().numpy().copy())
+                    al_by_k[K] = float(np.concatenate(als).mean())
+                bytes_ = sum(act) * expert_bytes + L * E * d * 2 + V * d * 2 + M * d * 4 + \
+                    2 * M * V * 4 + (B * K * V * 4 if K else 0)
+                times.setdefault(M, []).append(ms)
+                rec = {"moe": w.name, "sigma": sigma, "B": B, "K": K, "M": M, "ms_per_step": ms,
+                       "active_experts_per_block": act,
+                       "expected_active_uniform": om.expected_active(E, w.top_k, M),
+                       "step_bytes": bytes_, "step_hbm_frac": bytes_ / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
+                       "verified_positions_per_s": M / (ms / 1e3),
+                       "launch": "hipgraph" if a.graph else "eager"}
+                points.append(rec)
+                print(json.dumps(rec), flush=True)
+                del hidden, zq, x, logits, fws, aws
+        m_rows = sorted(times)
+        t_verif = [float(np.mean(times[m])) for m in m_rows]
+        al = [al_by_k[k] for k in MOE_K]
+        res = {"moe_k_table": w.name, "sigma": sigma, "al_measured": al, "rows": m_rows,
+               "t_verif_ms": t_verif, "choice": {}}
+        for c in K_TABLE_DRAFT_C:
+            t_b = {B: float(np.interp(B, m_rows, t_verif)) for B in MOE_B}
+            draft = [[c * K * t_b[B] for K in MOE_K] for B in MOE_B]
+            k, gp = sv.choose_k(m_rows, t_verif, al, list(MOE_B), draft)
+            res["choice"][f"c={c}"] = {str(B): {"K": int(k[i]), "speedup_vs_K0": float(gp[i] * t_b[B])}
+                                       for i, B in enumerate(MOE_B)}
+        print(json.dumps(res), flush=True)
+        del target, drafter, pr, pu, pd
+        torch.cuda.empty_cache()
+
+
+def cpu_ints(t):
+    return [int(v) for v in t.cpu().tolist()]
+
+
 ATTN_K = (0, 1, 3, 7, 15)
 
 
@@ -525,6 +616,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--moe", action="store_true",
+                    help="mixture-of-experts target: step time, experts touched and HBM roofline per "
+                         "B x K, and the goodput-optimal draft length per batch size")
     ap.add_argument("--attention", action="store_true",
                     help="paged attention of the verified positions: time and HBM roofline per "
                          "workload and draft length")
@@ -561,6 +655,9 @@ def main():
         return
     if a.attention:
         _attention_bench(a)
+        return
+    if a.moe:
+        _moe_bench(a)
         return
     if a.crossover:
         # forward-only time per row count with each MFMA family forced: the

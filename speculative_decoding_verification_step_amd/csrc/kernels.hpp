@@ -61,6 +61,19 @@ hipError_t launch_rmsnorm(const float* src, float* hout, const float* part, int 
                           const float* gain, void* act, int M, int d, float eps, int bf16,
                           int act_tiled, hipStream_t stream);
 
+// Weighted expert outputs of a mixture-of-experts block, folded into the
+// residual stream by the next RMSNorm: h[t] += sum_j wts[t k + j] *
+// Y[inv[t k + j]], j = 0 .. k - 1 in rank order (Y [M k, d] fp32).
+constexpr int kMoeFoldMaxK = 8;
+struct MoeFold {
+    const float* Y = nullptr;
+    const float* wts = nullptr;
+    const int32_t* inv = nullptr;
+    int k = 0;
+};
+hipError_t launch_rmsnorm_moe(float* h, const MoeFold& fold, const float* gain, void* act, int M,
+                              int d, float eps, int act_tiled, hipStream_t stream);
+
 // Split count of the LDS-staged GEMM's K range for an [M, N, K] product
 // (so that the tile grid fills the chip).
 int tiled_splits(int M, int N, int K);

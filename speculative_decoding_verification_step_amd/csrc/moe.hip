@@ -1,19 +1,19 @@
 // Verification forward of a mixture-of-experts target (C ABI in
 // include/spec_verify_moe.h).
 //
-// Per block: RMSNorm -> router (streaming MFMA matmul, [M, E] scores) ->
-// routing (one workgroup: top_k per position, softmax weights, and a
-// counting sort of the M * top_k (position, slot) pairs by expert, in
-// position order, so every expert's rows are one contiguous range) ->
-// grouped up projection (+ SiLU) -> grouped down projection -> combine
-// (h += sum over slots, in rank order, of weight * expert output).  The
+// Per block: RMSNorm -> router scores -> top_k per position (ties to the
+// lower id, softmax weights) -> counting sort of the M * top_k (position,
+// slot) pairs by expert, so every expert's rows are one contiguous range ->
+// grouped up projection (+ SiLU) -> grouped down projection -> the next
+// RMSNorm, which first adds the weighted expert outputs to the residual
+// stream (slots in rank order).  The
 // grouped kernels give every (expert, 16-row weight fragment) a workgroup
 // that returns before touching memory when the expert has no rows, so a step
 // streams the weights of the experts it uses and nothing else - the effect
 // the pages attribute to MoE verification (Cohere, "Dynamic speculative
 // decoding"): more verified positions, more experts loaded.  The matmul core
 // is the streaming one of the dense path: weight fragments from HBM straight
-// into registers as the A operand of v_mfma_f32_16x16x32_bf16, eight waves
+// into registers as the A operand of v_mfma_f32_16x16x32_bf16, four waves
 // splitting the reduction, a fixed-order LDS sum.
 #include <float.h>
 #include <math.h>
@@ -40,101 +40,270 @@ constexpr int kMoeMaxRows = 1024;     // positions per call (routing in one work
 constexpr int kMoeMaxExperts = 256;
 constexpr int kMoeMaxTopK = 8;
 constexpr int kRouteThreads = 1024;
-constexpr int kRouteChunk = 32;       // positions per counting chunk
-constexpr int kGroupWaves = 8;        // k slices of a grouped workgroup
-constexpr int kGroupSteps = 2;        // 32-wide k steps per buffer
+constexpr int kGroupWaves = 4;        // k slices of a grouped workgroup
 
 // ---- routing ------------------------------------------------------------------
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const float* __restrict__ z, int M, int E, int k, int32_t* __restrict__ sel_out,
-    float* __restrict__ wts, int32_t* __restrict__ offs, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ active) {
-    __shared__ int32_t lsel[kMoeMaxRows * kMoeMaxTopK];
-    __shared__ int32_t cnt[kMoeMaxRows / kRouteChunk][kMoeMaxExperts];
-    __shared__ int32_t loff[kMoeMaxExperts + 1];
-    const int tid = threadIdx.x;
-    const int nchunk = (M + kRouteChunk - 1) / kRouteChunk;
+constexpr int kRouterWaves = 4;
+constexpr int kMaxRouterSplits = 16;
 
-    // top_k of each position: k passes of an argmax over the unchosen experts
-    // (strict >: the lower id wins ties), then softmax over the chosen scores
-    for (int t = tid; t < M; t += kRouteThreads) {
-        const float* zr = z + (size_t)t * E;
-        uint32_t taken[kMoeMaxExperts / 32];
+// Router scores, split three ways so that any M fills the chip: workgroup
+// (fe, ks, mb) takes experts 16 fe .. 16 fe + 15, reduction steps (32 wide)
+// ks * spw .. ks * spw + spw - 1 and positions 64 mb .. 64 mb + 63, and
+// writes part[ks][t][e].  A wave holds one weight fragment per step (A
+// operand) and runs the 16-position fragments of activations through it;
+// the four waves' sums are added in LDS in wave order.
+__device__ __forceinline__ void router_partial(const uint16_t* __restrict__ a,
+                                               const uint16_t* __restrict__ Wr, int M, int E, int d,
+                                               int spw, int fe, int ks, int m0,
+                                               float* __restrict__ part,
+                                               float (*red)[4][4][kWave]) {
+    constexpr int MF = 4;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int S = d / 32;
+    const int s0 = ks * spw, s1 = min(S, s0 + spw);
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    f32x4v acc[MF];
 #pragma unroll
-        for (int w = 0; w < kMoeMaxExperts / 32; ++w) taken[w] = 0u;
-        float zs[kMoeMaxTopK];
-        int es[kMoeMaxTopK];
-        for (int j = 0; j < k; ++j) {
-            float best = -INFINITY;
-            int bi = -1;
-            for (int e = 0; e < E; ++e) {
-                if (taken[e >> 5] & (1u << (e & 31))) continue;
-                const float v = zr[e] == zr[e] ? zr[e] : -INFINITY;   // NaN ranks last
-                if (bi < 0 || v > best) {
-                    best = v;
-                    bi = e;
+    for (int mf = 0; mf < MF; ++mf) acc[mf] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int s = s0 + wave; s < s1; s += kRouterWaves) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(Wr + ((size_t)fe * S + s) * 512 + lane * 8);
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+            const int t = m0 + mf * 16 + r16;
+            const bf16x8 x = t < M ? *reinterpret_cast<const bf16x8*>(a + (size_t)t * d + 32 * s + 8 * g)
+                                   : zero8;
+            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc[mf], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][mf][r][lane] = acc[mf][r];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 256 * MF; i += kRouterWaves * kWave) {
+        const int ii = i & 15, jj = (i >> 4) & 15, mf = i >> 8;   // expert ii, position jj
+        const int e = fe * 16 + ii, t = m0 + mf * 16 + jj;
+        if (e >= E || t >= M) continue;
+        const int r = ii & 3, l = ((ii >> 2) << 4) + jj;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kRouterWaves; ++w) v += red[w][mf][r][l];
+        part[((size_t)ks * M + t) * E + e] = v;
+    }
+}
+
+// Scores of `rows` positions t0 .. t0 + rows - 1 into LDS: zs[r][e] (row
+// stride Ep, a multiple of 4) = the partial planes added in split order; a
+// NaN score, and the padding columns e >= E, become -inf.  A thread loads
+// all planes of up to 4 (position, expert) pairs at once.
+template <int THREADS>
+__device__ __forceinline__ void sum_planes(const float* __restrict__ part, int KS, int M, int E,
+                                           int Ep, int t0, int rows, float* zs) {
+    constexpr int P = 4;
+    const int n = rows * Ep;
+    for (int i0 = 0; i0 < n; i0 += P * THREADS) {
+        float pv[P][kMaxRouterSplits];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = i0 + p * THREADS + (int)threadIdx.x;
+            const int r = i / Ep, e = i - r * Ep;
+            const bool in = i < n && e < E;
+#pragma unroll
+            for (int y = 0; y < kMaxRouterSplits; ++y)
+                pv[p][y] = (in && y < KS) ? part[((size_t)y * M + t0 + r) * E + e] : 0.f;
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = i0 + p * THREADS + (int)threadIdx.x;
+            if (i >= n) continue;
+            const int e = i % Ep;
+            float z = 0.f;
+#pragma unroll
+            for (int y = 0; y < kMaxRouterSplits; ++y)
+                if (y < KS) z += pv[p][y];
+            zs[i] = (e < E && z == z) ? z : -INFINITY;
+        }
+    }
+}
+
+// Maximum of v over the wave, in every lane: DPP exchanges within rows of
+// 16 lanes (quad swaps, half-row and row mirrors), then the four row
+// maxima through readlane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_all(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));         // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));         // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f32<0x141>(v));        // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));        // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// top_k of the rows of zs, one wave per row (rows wave, wave + nwaves, ...):
+// k rounds of a wave-wide maximum over the experts not yet taken, the
+// lowest expert id among those equal to it (ballot, first set bit) taken;
+// the weights are the softmax of the chosen scores, summed in rank order.
+template <int THREADS>
+__device__ __forceinline__ void topk_rows(const float* zs, int rows, int E, int Ep, int k, int t0,
+                                          int32_t* __restrict__ sel, float* __restrict__ wts) {
+    constexpr int Q = kMoeMaxExperts / kWave;   // experts lane + 64 j
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int r = wave; r < rows; r += THREADS / kWave) {
+        float v[Q];
+        unsigned avail = 0;
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const int id = lane + kWave * j;
+            v[j] = id < E ? zs[r * Ep + id] : -INFINITY;
+            if (id < E) avail |= 1u << j;
+        }
+        float zsel[kMoeMaxTopK];
+        int esel[kMoeMaxTopK];
+#pragma unroll
+        for (int q = 0; q < kMoeMaxTopK; ++q) {
+            zsel[q] = 0.f;
+            esel[q] = 0;
+            if (q >= k) continue;
+            float m = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < Q; ++j)
+                if ((avail >> j) & 1u) m = fmaxf(m, v[j]);
+            m = wave_max_all(m);
+            int id = -1;
+#pragma unroll
+            for (int j = 0; j < Q; ++j) {
+                const unsigned long long b = __ballot(((avail >> j) & 1u) && v[j] == m);
+                if (id < 0 && b) id = kWave * j + __ffsll((long long)b) - 1;
+            }
+            if ((id & (kWave - 1)) == lane) avail &= ~(1u << (id / kWave));
+            zsel[q] = m;
+            esel[q] = id;
+        }
+        if (lane == 0) {
+            const int t = t0 + r;
+            float ex[kMoeMaxTopK], sum = 0.f;
+#pragma unroll
+            for (int q = 0; q < kMoeMaxTopK; ++q) {
+                ex[q] = q < k ? (zsel[0] == -INFINITY ? 1.f : expf(zsel[q] - zsel[0])) : 0.f;   // no number: equal
+                sum += ex[q];
+            }
+#pragma unroll
+            for (int q = 0; q < kMoeMaxTopK; ++q) {
+                if (q < k) {
+                    sel[t * k + q] = esel[q];
+                    wts[t * k + q] = ex[q] / sum;
                 }
             }
-            taken[bi >> 5] |= 1u << (bi & 31);
-            es[j] = bi;
-            zs[j] = best;
-        }
-        float sum = 0.f, ex[kMoeMaxTopK];
-        for (int j = 0; j < k; ++j) {
-            ex[j] = zs[0] == -INFINITY ? 1.f : expf(zs[j] - zs[0]);   // no finite score: equal
-            sum += ex[j];
-        }
-        for (int j = 0; j < k; ++j) {
-            sel_out[t * k + j] = es[j];
-            wts[t * k + j] = ex[j] / sum;
-            lsel[t * k + j] = es[j];
         }
     }
-    for (int i = tid; i < nchunk * E; i += kRouteThreads) cnt[i / E][i % E] = 0;
+}
+
+// Counting sort of the M * k (position, slot) pairs (expert ids in lsel, in
+// LDS) by expert, so every expert's rows are one contiguous range: counts by
+// LDS atomics, an exclusive scan over experts (one wave), then every pair
+// takes the next free row of its expert by LDS atomics.  The order of an
+// expert's rows is therefore not fixed, and nothing depends on it: every
+// output row of the grouped kernels is its own dot products, and the fold
+// finds each pair's row through inv.  Also lists the experts with rows in
+// id order (alist[0 .. *nact - 1]) for the grouped kernels.  cnt, loff: LDS
+// [E] and [E + 1].
+template <int THREADS>
+__device__ __forceinline__ void sort_pairs(const int32_t* lsel, int M, int E, int k, int32_t* cnt,
+                                           int32_t* loff, int32_t* __restrict__ offs,
+                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                           int32_t* __restrict__ alist, int32_t* __restrict__ nact,
+                                           int32_t* __restrict__ active) {
+    const int tid = threadIdx.x, n = M * k;
+    for (int x = tid; x < E; x += THREADS) cnt[x] = 0;
     __syncthreads();
-    // per-chunk counts (one thread per chunk, so no atomics)
-    if (tid < nchunk) {
-        const int t1 = min(M, (tid + 1) * kRouteChunk);
-        for (int t = tid * kRouteChunk; t < t1; ++t)
-            for (int j = 0; j < k; ++j) cnt[tid][lsel[t * k + j]] += 1;
-    }
+    for (int i = tid; i < n; i += THREADS) atomicAdd(&cnt[lsel[i]], 1);
     __syncthreads();
-    if (tid < E) {
-        int tot = 0;
-        for (int c = 0; c < nchunk; ++c) tot += cnt[c][tid];
-        loff[tid + 1] = tot;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        loff[0] = 0;
-        int used = 0;
-        for (int e = 0; e < E; ++e) {
-            used += loff[e + 1] > 0;
-            loff[e + 1] += loff[e];
+    if (tid < kWave) {                       // exclusive scan over experts, one wave
+        constexpr int Q = kMoeMaxExperts / kWave;   // experts Q * lane .. Q * lane + Q - 1
+        int c[Q], tot = 0, nz = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int x = Q * tid + q;
+            c[q] = x < E ? cnt[x] : 0;
+            tot += c[q];
+            nz += c[q] > 0;
         }
-        if (active) *active = used;
-    }
-    __syncthreads();
-    // chunk counts -> chunk start positions inside each expert's range
-    if (tid < E) {
-        int base = loff[tid];
-        for (int c = 0; c < nchunk; ++c) {
-            const int n = cnt[c][tid];
-            cnt[c][tid] = base;
-            base += n;
-        }
-    }
-    if (tid <= E) offs[tid] = loff[tid];
-    __syncthreads();
-    if (tid < nchunk) {
-        const int t1 = min(M, (tid + 1) * kRouteChunk);
-        for (int t = tid * kRouteChunk; t < t1; ++t)
-            for (int j = 0; j < k; ++j) {
-                const int pos = cnt[tid][lsel[t * k + j]]++;
-                perm[pos] = t * k + j;
-                inv[t * k + j] = pos;
+        int itot = tot, inz = nz;            // inclusive scans across lanes
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int a1 = __shfl_up(itot, o, kWave), a2 = __shfl_up(inz, o, kWave);
+            if (tid >= o) {
+                itot += a1;
+                inz += a2;
             }
+        }
+        int base = itot - tot, slot = inz - nz;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int x = Q * tid + q;
+            if (x < E) {
+                loff[x] = base;
+                base += c[q];
+                if (c[q] > 0) alist[slot++] = x;
+            }
+        }
+        if (tid == kWave - 1) {
+            loff[E] = itot;
+            *nact = inz;
+            if (active) *active = inz;
+        }
     }
+    __syncthreads();
+    for (int x = tid; x <= E; x += THREADS) {
+        offs[x] = loff[x];
+        if (x < E) cnt[x] = loff[x];         // next free row of expert x
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += THREADS) {
+        const int pos = atomicAdd(&cnt[lsel[i]], 1);
+        perm[pos] = i;
+        inv[i] = pos;
+    }
+}
+
+__global__ __launch_bounds__(kRouterWaves * kWave) void moe_router_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ Wr, int M, int E, int d, int spw,
+    float* __restrict__ part) {
+    __shared__ float red[kRouterWaves][4][4][kWave];
+    router_partial(a, Wr, M, E, d, spw, blockIdx.x, blockIdx.y, blockIdx.z * 64, part, red);
+}
+
+// top_k of positions 4 blockIdx.x .. 4 blockIdx.x + 3, one wave each.
+__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ part, int KS, int M,
+                                                       int E, int Ep, int k,
+                                                       int32_t* __restrict__ sel,
+                                                       float* __restrict__ wts) {
+    __shared__ float zs[4 * kMoeMaxExperts];
+    const int t0 = blockIdx.x * 4;
+    const int rows = min(4, M - t0);
+    sum_planes<256>(part, KS, M, E, Ep, t0, rows, zs);
+    __syncthreads();
+    topk_rows<256>(zs, rows, E, Ep, k, t0, sel, wts);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_sort_kernel(
+    const int32_t* __restrict__ sel, int M, int E, int k, int32_t* __restrict__ offs,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ alist,
+    int32_t* __restrict__ nact, int32_t* __restrict__ active) {
+    __shared__ int32_t lsel[kMoeMaxRows * kMoeMaxTopK];
+    __shared__ int32_t cnt[kMoeMaxExperts];
+    __shared__ int32_t loff[kMoeMaxExperts + 1];
+    for (int i = threadIdx.x; i < M * k; i += kRouteThreads) lsel[i] = sel[i];
+    __syncthreads();
+    sort_pairs<kRouteThreads>(lsel, M, E, k, cnt, loff, offs, perm, inv, alist, nact, active);
 }
 
 // ---- grouped matmul -------------------------------------------------------------
@@ -142,29 +311,51 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
 // e (offs[e] .. offs[e+1]); src(row) = perm[row] / top_k (gather of the
 // positions' activations) when `gather`, else row.  W_e = W + e * wstride, in
 // the tiled layout.  Epilogue: SiLU + bf16 (up) or fp32 store (down).
-template <int EPI>
+// Workgroup i takes listed expert alist[i / nfr] and the RF 16-row weight
+// fragments RF * (i % nfr) .. + RF - 1; workgroups past the *nact listed
+// experts return at once.  A wave streams its k slice of those fragments in
+// buffers of U 32-wide steps, the first issued before the row indices are
+// read, and runs MF 16-row activation fragments per pass over the expert's
+// rows through them (one activation load serves RF weight fragments;
+// fragments past the expert's rows are skipped by the whole wave).
+template <int EPI, int MF, int U, int RF>
 __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
     const uint16_t* __restrict__ W, size_t wstride, int N, int K, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ perm, int gather, int top_k, const int32_t* __restrict__ offs,
-    void* __restrict__ out) {
-    constexpr int MF = 4, U = kGroupSteps;
+    const int32_t* __restrict__ alist, const int32_t* __restrict__ nact, void* __restrict__ out) {
     const int nfrag = (N + 15) / 16;
-    const int e = blockIdx.x / nfrag;
-    const int frag = blockIdx.x % nfrag;
-    const int row0 = offs[e];
-    const int rows = offs[e + 1] - row0;
-    if (rows <= 0) return;                 // an idle expert reads nothing
+    const int nfr = (nfrag + RF - 1) / RF;
+    const int li = blockIdx.x / nfr;
+    const int f0 = (blockIdx.x % nfr) * RF;
+    if (li >= *nact) return;               // fewer experts in use than the launch allows
+    const int e = alist[li];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int r16 = lane & 15, g = lane >> 4;
     const int S = K / 32;
     const int s0 = S * wave / kGroupWaves, s1 = S * (wave + 1) / kGroupWaves;
-    const uint16_t* wrow = W + (size_t)e * wstride + ((size_t)frag * S) * 512 + lane * 8;
+    const uint16_t* wbase = W + (size_t)e * wstride + lane * 8;
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    __shared__ float red[kGroupWaves][MF][4][kWave];
+    __shared__ float red[kGroupWaves][RF][MF][4][kWave];
+
+    bf16x8 wa[U][RF], wb[U][RF], xa[U][MF], xb[U][MF];
+    auto loadw = [&](bf16x8 (&w)[U][RF], int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf)
+                w[u][rf] = (s + u < s1 && f0 + rf < nfrag)
+                               ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(
+                                     wbase + ((size_t)(f0 + rf) * S + s + u) * 512))
+                               : zero8;
+    };
+    loadw(wa, s0);                          // weights first: they need no row index
+    const int row0 = offs[e];
+    const int rows = offs[e + 1] - row0;
 
     for (int pass = 0; pass < rows; pass += 16 * MF) {
+        const int prow = rows - pass;      // rows left, > 0
         const uint16_t* arow[MF];
         bool aval[MF];
 #pragma unroll
@@ -175,53 +366,58 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
             const int src = gather ? perm[rr] / top_k : rr;
             arow[mf] = act + (size_t)src * K + 8 * g;
         }
-        f32x4v acc[MF];
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) acc[mf] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        bf16x8 wa[U], wb[U], xa[U][MF], xb[U][MF];
-        auto load = [&](bf16x8 (&w)[U], bf16x8 (&x)[U][MF], int s) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int ss = s + u;
-                const bool in = ss < s1;
-#pragma unroll
-                for (int mf = 0; mf < MF; ++mf)
-                    x[u][mf] = (in && aval[mf]) ? *reinterpret_cast<const bf16x8*>(arow[mf] + 32 * ss)
-                                                : zero8;
-                w[u] = in ? __builtin_nontemporal_load(
-                                reinterpret_cast<const bf16x8*>(wrow + (size_t)512 * ss))
-                          : zero8;
-            }
-        };
-        auto compute = [&](const bf16x8 (&w)[U], const bf16x8 (&x)[U][MF]) {
+        auto loadx = [&](bf16x8 (&x)[U][MF], int s) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int mf = 0; mf < MF; ++mf)
-                    acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[u], x[u][mf], acc[mf], 0, 0, 0);
+                    x[u][mf] = (s + u < s1 && aval[mf])
+                                   ? *reinterpret_cast<const bf16x8*>(arow[mf] + 32 * (s + u))
+                                   : zero8;
         };
-        load(wa, xa, s0);
+        f32x4v acc[RF][MF];
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) acc[rf][mf] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](const bf16x8 (&w)[U][RF], const bf16x8 (&x)[U][MF]) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf)
+                    if (mf == 0 || mf * 16 < prow)
+#pragma unroll
+                        for (int rf = 0; rf < RF; ++rf)
+                            acc[rf][mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                w[u][rf], x[u][mf], acc[rf][mf], 0, 0, 0);
+        };
+        if (pass) loadw(wa, s0);
+        loadx(xa, s0);
         for (int s = s0; s < s1; s += 2 * U) {
-            load(wb, xb, s + U);
+            loadw(wb, s + U);
+            loadx(xb, s + U);
             compute(wa, xa);
-            load(wa, xa, s + 2 * U);
+            loadw(wa, s + 2 * U);
+            loadx(xa, s + 2 * U);
             compute(wb, xb);
         }
         if (pass) __syncthreads();         // the previous pass's readers are done
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
+        for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][mf][r][lane] = acc[mf][r];
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wave][rf][mf][r][lane] = acc[rf][mf][r];
         __syncthreads();
-        for (int i = threadIdx.x; i < 256 * MF; i += kGroupWaves * kWave) {
-            const int ii = i & 15, jj = (i >> 4) & 15, mf = i >> 8;
-            const int n = frag * 16 + ii;
+        for (int i = threadIdx.x; i < 256 * MF * RF; i += kGroupWaves * kWave) {
+            const int ii = i & 15, jj = (i >> 4) & 15, mf = (i >> 8) % MF, rf = (i >> 8) / MF;
+            const int n = (f0 + rf) * 16 + ii;
             const int j = pass + mf * 16 + jj;
             if (n >= N || j >= rows) continue;
             const int r = ii & 3, l = ((ii >> 2) << 4) + jj;
             float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < kGroupWaves; ++w) v += red[w][mf][r][l];
+            for (int w = 0; w < kGroupWaves; ++w) v += red[w][rf][mf][r][l];
             const size_t o = (size_t)(row0 + j) * N + n;
             if constexpr (EPI == kEpiSilu)
                 static_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(silu(v));
@@ -231,42 +427,33 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
     }
 }
 
-// h[t] += sum_j wts[t, j] * Y[inv[t * k + j]]   (slots in rank order)
-__global__ __launch_bounds__(256) void moe_combine_kernel(
-    float* __restrict__ h, const float* __restrict__ Y, const float* __restrict__ wts,
-    const int32_t* __restrict__ inv, int M, int d, int k) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;   // (t, 4-column group)
-    const int d4 = d / 4;
-    if (i >= (long long)M * d4) return;
-    const int t = (int)(i / d4), c = (int)(i % d4);
-    f32x4v acc = *reinterpret_cast<const f32x4v*>(h + (size_t)t * d + 4 * c);
-    f32x4v y = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j)
-        y += wts[t * k + j] * *reinterpret_cast<const f32x4v*>(Y + (size_t)inv[t * k + j] * d + 4 * c);
-    *reinterpret_cast<f32x4v*>(h + (size_t)t * d + 4 * c) = acc + y;
-}
-
 // ---- host plan --------------------------------------------------------------
 constexpr size_t kAlign = 256;
 size_t aup(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MoePlan {
     int head_kind = kMfmaSkinny;
-    size_t off_h, off_a, off_z, off_sel, off_w, off_offs, off_perm, off_inv, off_s, off_y, bytes;
+    int router_spw = 0, router_splits = 0;   // reduction steps per router split, splits
+    size_t off_h, off_a, off_part, off_sel, off_w, off_offs, off_list, off_perm, off_inv, off_s,
+        off_y, bytes;
 };
 
 MoePlan plan_moe(const sv_moe_desc& d, int M) {
     MoePlan p{};
     const size_t Mk = (size_t)M * d.top_k;
     p.head_kind = M >= 65 ? kMfmaTiled : kMfmaSkinny;
+    const int S = d.d / 32;
+    p.router_spw = S / 16 > 8 ? (S + 15) / 16 : 8;    // at most 16 partial score planes
+    p.router_splits = (S + p.router_spw - 1) / p.router_spw;
     const size_t arows = (size_t)(M + 15) / 16 * 16;
     size_t o = 0;
     p.off_h = o; o = aup(o + (size_t)M * d.d * 4);
     p.off_a = o; o = aup(o + arows * d.d * 2);
-    p.off_z = o; o = aup(o + (size_t)M * d.n_experts * 4);
+    p.off_part = o; o = aup(o + (size_t)p.router_splits * M * d.n_experts * 4);
     p.off_sel = o; o = aup(o + Mk * 4);
     p.off_w = o; o = aup(o + Mk * 4);
-    p.off_offs = o; o = aup(o + (size_t)(d.n_experts + 1) * 4);
+    p.off_offs = o; o = aup(o + (size_t)(d.n_experts + 2) * 4);   // offsets, then the count
+    p.off_list = o; o = aup(o + (size_t)d.n_experts * 4);
     p.off_perm = o; o = aup(o + Mk * 4);
     p.off_inv = o; o = aup(o + Mk * 4);
     p.off_s = o; o = aup(o + Mk * d.ffn * 2);
@@ -277,6 +464,31 @@ MoePlan plan_moe(const sv_moe_desc& d, int M) {
 
 int moe_hip_fail(hipError_t e, const char* what) {
     return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// One grouped projection.  The arrangement follows the rows an expert holds
+// on average (M * top_k / E): few rows want many workgroups and deep weight
+// buffers; many rows want each activation load shared by several weight
+// fragments (measured on the 64-expert top-6 workload over M = 1 .. 576).
+template <int EPI>
+void launch_grouped(ProfScope& prof, int M, int E, int k, int listed, int nfrag, hipStream_t s,
+                    const uint16_t* W, size_t wstride, int N, int K, const uint16_t* act,
+                    const int32_t* perm, int gather, const int32_t* offs, const int32_t* alist,
+                    const int32_t* nact, void* out) {
+#define SV_GROUPED(MF, U, RF)                                                                      \
+    SV_LAUNCH(prof, (moe_grouped_kernel<EPI, MF, U, RF>),                                         \
+              (unsigned)(listed * ((nfrag + RF - 1) / RF)), kGroupWaves * kWave, s, W, wstride, N, \
+              K, act, perm, gather, k, offs, alist, nact, out)
+    const int mean_rows = (M * k + E - 1) / E;
+    if (M <= 16)
+        SV_GROUPED(1, 4, 1);      // at most 16 rows per expert
+    else if (mean_rows <= 8)
+        SV_GROUPED(1, 4, 2);
+    else if (mean_rows <= 16)
+        SV_GROUPED(2, 2, 2);
+    else
+        SV_GROUPED(4, 1, 4);
+#undef SV_GROUPED
 }
 
 }  // namespace
@@ -331,10 +543,12 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
     char* w = static_cast<char*>(ws);
     float* h = reinterpret_cast<float*>(w + p.off_h);
     void* a = w + p.off_a;
-    float* z = reinterpret_cast<float*>(w + p.off_z);
     int32_t* sel = reinterpret_cast<int32_t*>(w + p.off_sel);
     float* wts = reinterpret_cast<float*>(w + p.off_w);
+    float* part = reinterpret_cast<float*>(w + p.off_part);
     int32_t* offs = reinterpret_cast<int32_t*>(w + p.off_offs);
+    int32_t* nact = offs + d.n_experts + 1;
+    int32_t* alist = reinterpret_cast<int32_t*>(w + p.off_list);
     int32_t* perm = reinterpret_cast<int32_t*>(w + p.off_perm);
     int32_t* inv = reinterpret_cast<int32_t*>(w + p.off_inv);
     void* S = w + p.off_s;
@@ -345,57 +559,65 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
     const size_t down_stride = tiled_elems(d.d, d.ffn);
     hipError_t e;
 
-    e = launch_rmsnorm(hidden, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, 1, 0, s);
+    e = launch_rmsnorm(hidden, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, 1,
+                       d.n_layers == 0 && p.head_kind == kMfmaTiled, s);
     if (e != hipSuccess) return moe_hip_fail(e, "rmsnorm launch");
     for (int l = 0; l < d.n_layers; ++l) {
-        MatmulArgs r{};
-        r.W = static_cast<const uint16_t*>(d.w_router) + (size_t)l * router_stride;
-        r.act = a;
-        r.M = M; r.N = E; r.K = d.d;
-        r.epi = kEpiStore; r.out = z; r.bf16 = 1; r.tiled = 1;
-        r.name = "moe_router";
-        e = launch_matmul(r, kMfmaSkinny, s);
-        if (e != hipSuccess) return moe_hip_fail(e, "router launch");
+        const uint16_t* wr = static_cast<const uint16_t*>(d.w_router) + (size_t)l * router_stride;
+        int32_t* act_out = active_experts ? active_experts + l : nullptr;
+        const int Ep = (E + 3) & ~3;
         {
-            ProfScope prof("moe_route", s, (double)M * E * 4, 0.0);
-            SV_LAUNCH(prof, moe_route_kernel, 1, kRouteThreads, s, z, M, E, k, sel, wts, offs, perm,
-                      inv, active_experts ? active_experts + l : nullptr);
+            ProfScope prof("moe_router", s, (double)E * d.d * 2 + (double)M * d.d * 2,
+                           2.0 * M * E * (double)d.d);
+            const dim3 grid((unsigned)((E + 15) / 16), (unsigned)p.router_splits,
+                            (unsigned)((M + 63) / 64));
+            SV_LAUNCH(prof, moe_router_kernel, grid, kRouterWaves * kWave, s,
+                      static_cast<const uint16_t*>(a), wr, M, E, d.d, p.router_spw, part);
             e = hipGetLastError();
-            if (e != hipSuccess) return moe_hip_fail(e, "route launch");
+            if (e != hipSuccess) return moe_hip_fail(e, "router launch");
         }
+        {
+            ProfScope prof("moe_topk", s, (double)p.router_splits * M * E * 4, 0.0);
+            SV_LAUNCH(prof, moe_topk_kernel, (unsigned)((M + 3) / 4), 256, s, part,
+                      p.router_splits, M, E, Ep, k, sel, wts);
+            e = hipGetLastError();
+            if (e != hipSuccess) return moe_hip_fail(e, "top-k launch");
+        }
+        {
+            ProfScope prof("moe_sort", s, (double)M * k * 12, 0.0);
+            SV_LAUNCH(prof, moe_sort_kernel, 1, kRouteThreads, s, sel, M, E, k, offs, perm, inv,
+                      alist, nact, act_out);
+            e = hipGetLastError();
+            if (e != hipSuccess) return moe_hip_fail(e, "sort launch");
+        }
+        const int listed = E < M * k ? E : M * k;   // experts a block can use
         {
             // bytes depend on the experts the device picks: counted by the caller
             ProfScope prof("moe_up_silu", s, 0.0, 2.0 * M * k * (double)d.ffn * d.d);
-            const unsigned grid = (unsigned)(E * ((d.ffn + 15) / 16));
-            SV_LAUNCH(prof, moe_grouped_kernel<kEpiSilu>, grid, kGroupWaves * kWave, s,
-                      static_cast<const uint16_t*>(d.w_up) + (size_t)l * E * up_stride, up_stride,
-                      d.ffn, d.d, static_cast<const uint16_t*>(a), perm, 1, k, offs, S);
+            launch_grouped<kEpiSilu>(prof, M, E, k, listed, (d.ffn + 15) / 16, s,
+                                     static_cast<const uint16_t*>(d.w_up) + (size_t)l * E * up_stride,
+                                     up_stride, d.ffn, d.d, static_cast<const uint16_t*>(a), perm, 1,
+                                     offs, alist, nact, S);
             e = hipGetLastError();
             if (e != hipSuccess) return moe_hip_fail(e, "grouped up launch");
         }
         {
             ProfScope prof("moe_down", s, 0.0, 2.0 * M * k * (double)d.ffn * d.d);
-            const unsigned grid = (unsigned)(E * ((d.d + 15) / 16));
-            SV_LAUNCH(prof, moe_grouped_kernel<kEpiStore>, grid, kGroupWaves * kWave, s,
-                      static_cast<const uint16_t*>(d.w_down) + (size_t)l * E * down_stride,
-                      down_stride, d.d, d.ffn, static_cast<const uint16_t*>(S), perm, 0, k, offs, Y);
+            launch_grouped<kEpiStore>(prof, M, E, k, listed, (d.d + 15) / 16, s,
+                                      static_cast<const uint16_t*>(d.w_down) +
+                                          (size_t)l * E * down_stride,
+                                      down_stride, d.d, d.ffn, static_cast<const uint16_t*>(S), perm,
+                                      0, offs, alist, nact, Y);
             e = hipGetLastError();
             if (e != hipSuccess) return moe_hip_fail(e, "grouped down launch");
         }
-        {
-            ProfScope prof("moe_combine", s, (double)M * d.d * (8.0 + 4.0 * k), 0.0);
-            const long long n = (long long)M * (d.d / 4);
-            SV_LAUNCH(prof, moe_combine_kernel, (unsigned)((n + 255) / 256), 256, s, h, Y, wts, inv,
-                      M, d.d, k);
-            e = hipGetLastError();
-            if (e != hipSuccess) return moe_hip_fail(e, "combine launch");
-        }
-        e = launch_rmsnorm(h, h, nullptr, 0, d.gain + (size_t)(l + 1) * d.d, a, M, d.d, d.rms_eps, 1,
-                           l + 1 == d.n_layers && p.head_kind == kMfmaTiled, s);
-        if (e != hipSuccess) return moe_hip_fail(e, "rmsnorm launch");
-    }
-    if (d.n_layers == 0 && p.head_kind == kMfmaTiled) {
-        e = launch_rmsnorm(h, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, 1, 1, s);
+        MoeFold fold;
+        fold.Y = Y;
+        fold.wts = wts;
+        fold.inv = inv;
+        fold.k = k;
+        e = launch_rmsnorm_moe(h, fold, d.gain + (size_t)(l + 1) * d.d, a, M, d.d, d.rms_eps,
+                               l + 1 == d.n_layers && p.head_kind == kMfmaTiled, s);
         if (e != hipSuccess) return moe_hip_fail(e, "rmsnorm launch");
     }
     MatmulArgs hd{};

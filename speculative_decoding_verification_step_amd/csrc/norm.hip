@@ -6,7 +6,10 @@
 // the row's loads are in flight at once, and the sum of squares is reduced
 // inside the workgroup in a fixed order.  When the previous down projection
 // left split-K partial planes, they are folded in first, in split order:
-// h = src + (part[0] + part[1] + ...), and h is written back.
+// h = src + (part[0] + part[1] + ...), and h is written back.  After a
+// mixture-of-experts block the weighted expert outputs are folded in the
+// same way: h = src + (w_0 Y[inv_0] + w_1 Y[inv_1] + ...), slots in rank
+// order.
 //
 // For the LDS-staged GEMM the bf16 activations are written in the matrix-core
 // operand layout (16 x 32 blocks of one KiB, as the tiled weights), rows
@@ -18,12 +21,12 @@ namespace sv {
 
 namespace {
 
-template <bool kBf16, int VPT, int THREADS>
+template <bool kBf16, bool kMoe, int VPT, int THREADS>
 __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     const float* src, float* hout,  // src may equal hout
     const float* __restrict__ part, int splits, size_t split_stride,
     const float* __restrict__ gain, void* __restrict__ act, int M, int d, float eps,
-    int act_tiled) {
+    int act_tiled, const MoeFold fold) {
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const size_t off = (size_t)row * d;
@@ -49,25 +52,61 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src + off);
 
     // the row and the gains are loaded together, so the gains do not add a
-    // second memory round trip after the reduction
+    // second memory round trip after the reduction (rows of more than 16384
+    // elements load the gains afterwards, to stay within the registers)
+    constexpr bool kHoldGain = VPT <= 4;
     const f32x4* g4 = reinterpret_cast<const f32x4*>(gain);
-    f32x4 h[VPT], g[VPT];
+    f32x4 h[VPT], g[kHoldGain ? VPT : 1];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = tid + v * THREADS;
         h[v] = c < n4 ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
-        g[v] = c < n4 ? g4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kHoldGain) g[v] = c < n4 ? g4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (splits > 0) {
+        // acc = part[0] + part[1] + ... per element, planes outermost
+        f32x4 acc[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int c = tid + v * THREADS;
-            if (c >= n4) continue;
-            f32x4 acc = reinterpret_cast<const f32x4*>(part + off)[c];
-            for (int s = 1; s < splits; ++s)
-                acc += reinterpret_cast<const f32x4*>(part + s * split_stride + off)[c];
-            h[v] += acc;
+            acc[v] = c < n4 ? reinterpret_cast<const f32x4*>(part + off)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll 1
+        for (int s = 1; s < splits; ++s) {
+            const f32x4* p4 = reinterpret_cast<const f32x4*>(part + s * split_stride + off);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                const int c = tid + v * THREADS;
+                if (c < n4) acc[v] += p4[c];
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) h[v] += acc[v];
+    }
+    if constexpr (kMoe) {
+        f32x4 y[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) y[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // slots in groups of JG, so that at most 16 vectors are in flight
+        constexpr int JG = VPT >= 16 ? 1 : 16 / VPT;
+#pragma unroll 1
+        for (int j0 = 0; j0 < fold.k; j0 += JG) {
+#pragma unroll
+            for (int jj = 0; jj < JG; ++jj) {
+                const int j = j0 + jj;
+                if (j >= fold.k) break;
+                const float wj = fold.wts[row * fold.k + j];
+                const f32x4* yr =
+                    reinterpret_cast<const f32x4*>(fold.Y + (size_t)fold.inv[row * fold.k + j] * d);
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    const int c = tid + v * THREADS;
+                    if (c < n4) y[v] += wj * yr[c];
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) h[v] += y[v];
     }
     float ss = 0.f;
 #pragma unroll
@@ -77,7 +116,7 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
         ss += h[v].z * h[v].z;
         ss += h[v].w * h[v].w;
     }
-    if (hout != src || splits > 0) {
+    if (hout != src || splits > 0 || kMoe) {
         f32x4* h4 = reinterpret_cast<f32x4*>(hout + off);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
@@ -99,8 +138,9 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     for (int v = 0; v < VPT; ++v) {
         const int c = tid + v * THREADS;
         if (c >= n4) continue;
-        const f32x4 y = {h[v].x * inv_rms * g[v].x, h[v].y * inv_rms * g[v].y,
-                         h[v].z * inv_rms * g[v].z, h[v].w * inv_rms * g[v].w};
+        const f32x4 gv = kHoldGain ? g[kHoldGain ? v : 0] : g4[c];
+        const f32x4 y = {h[v].x * inv_rms * gv.x, h[v].y * inv_rms * gv.y,
+                         h[v].z * inv_rms * gv.z, h[v].w * inv_rms * gv.w};
         if constexpr (kBf16) {
             uint2 packed;
             packed.x = f32_to_bf16(y.x) | (f32_to_bf16(y.y) << 16);
@@ -112,15 +152,16 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     }
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kMoe>
 hipError_t launch_norm_dtype(const float* src, float* hout, const float* part, int splits,
                              size_t stride, const float* gain, void* act, int M, int d, float eps,
-                             int act_tiled, hipStream_t stream, const ProfScope& prof) {
+                             int act_tiled, const MoeFold& fold, hipStream_t stream,
+                             const ProfScope& prof) {
     const int n4 = d / 4;
     const int rows = act_tiled ? (M + 15) / 16 * 16 : M;
-#define SV_NORM(VPT, T)                                                                       \
-    SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, VPT, T>), rows, T, stream, src, hout, part, splits, \
-              stride, gain, act, M, d, eps, act_tiled)
+#define SV_NORM(VPT, T)                                                                   \
+    SV_LAUNCH(prof, (rmsnorm_kernel<kBf16, kMoe, VPT, T>), rows, T, stream, src, hout, part, \
+              splits, stride, gain, act, M, d, eps, act_tiled, fold)
     if (n4 <= 256) SV_NORM(1, 256);
     else if (n4 <= 1024) SV_NORM(1, 1024);
     else if (n4 <= 2048) SV_NORM(2, 1024);
@@ -143,10 +184,21 @@ hipError_t launch_rmsnorm(const float* src, float* hout, const float* part, int 
         (double)M * d * (4.0 + 4.0 * splits + (writes_h ? 4.0 : 0.0) + (bf16 ? 2.0 : 4.0));
     ProfScope prof("rmsnorm", stream, bytes, 0.0);
     const size_t stride = (size_t)M * d;
-    return bf16 ? launch_norm_dtype<true>(src, hout, part, splits, stride, gain, act, M, d, eps,
-                                          act_tiled, stream, prof)
-                : launch_norm_dtype<false>(src, hout, part, splits, stride, gain, act, M, d, eps,
-                                           act_tiled, stream, prof);
+    const MoeFold none{};
+    return bf16 ? launch_norm_dtype<true, false>(src, hout, part, splits, stride, gain, act, M, d,
+                                                 eps, act_tiled, none, stream, prof)
+                : launch_norm_dtype<false, false>(src, hout, part, splits, stride, gain, act, M, d,
+                                                  eps, act_tiled, none, stream, prof);
+}
+
+hipError_t launch_rmsnorm_moe(float* h, const MoeFold& fold, const float* gain, void* act, int M,
+                              int d, float eps, int act_tiled, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    if (fold.k < 1 || fold.k > kMoeFoldMaxK || (act_tiled && d % 32)) return hipErrorInvalidValue;
+    const double bytes = (double)M * d * (4.0 + 4.0 * fold.k + 4.0 + 2.0);
+    ProfScope prof("rmsnorm_moe", stream, bytes, 0.0);
+    return launch_norm_dtype<true, true>(h, h, nullptr, 0, 0, gain, act, M, d, eps, act_tiled,
+                                         fold, stream, prof);
 }
 
 }  // namespace sv

@@ -60,6 +60,16 @@ def test_top1_and_all_experts():
 
 
 @gpu
+@pytest.mark.parametrize("M", [3, 40])
+def test_widest_router(M):
+    """256 experts, top-8 (the largest the library takes): every lane of a
+    top-k wave holds four experts."""
+    sv = require_gpu()
+    w = workload.MoEWorkload("moe-wide", 128, 64, 256, 8, 2, 333, 1, 4, 0.3, 1.0, 13)
+    _check(sv, w, workload.make_moe_model(w, draft_head=False), M, M + 256)
+
+
+@gpu
 def test_full_size_moe_rows():
     """The 64-expert top-6 stack at its benchmark size, B = 1, K = 4."""
     sv = require_gpu()
@@ -75,3 +85,29 @@ def test_moe_forward_is_deterministic():
     m = _device(sv, workload.make_moe_model(w, draft_head=False), 4)
     h = torch.from_numpy(np.random.default_rng(0).standard_normal((200, 256)).astype(np.float32)).cuda()
     assert torch.equal(m.forward(h), m.forward(h))
+
+
+@gpu
+@pytest.mark.parametrize("M", [7, 100])
+def test_exact_router_ties(M):
+    """Every expert of a block has the same router row, so all scores tie
+    exactly (in fp64 and in the kernel's fp32 alike): ties go to the lower
+    id, so experts 0 .. k-1 serve every position with equal weights.  No row
+    is set aside here: the rule decides, not the summation order.  M = 7
+    leaves a ragged top-k workgroup; M = 100 spans two router row blocks."""
+    sv = require_gpu()
+    for E, k in ((2, 1), (8, 3)):
+        w = workload.MoEWorkload("moe-ties", 128, 64, E, k, 2, 333, 1, 4, 0.3, 1.0, 11)
+        model = workload.make_moe_model(w, draft_head=False)
+        model["w_router"][:] = model["w_router"][:, :1]
+        m = _device(sv, model, k)
+        h = workload.make_hidden(workload.Workload("h", w.d, 1, 1, 1, "f32", 1, 1, 0, 1, "std_0.02",
+                                                   w.seed), M, sub=E)
+        active = torch.zeros(w.n_layers, dtype=torch.int32, device="cuda")
+        z = cpu(m.forward(torch.from_numpy(h).cuda(), active=active))
+        ref, _, used = om.forward(model, h, k)
+        assert [sorted(u) for u in used] == [list(range(k))] * w.n_layers
+        err = np.abs(z.astype(np.float64) - ref)
+        note(f"  ties E={E} k={k} M={M}: max |dlogit| {err.max():.3g}")
+        assert err.max() <= TOL_BF16
+        assert cpu(active).tolist() == [k] * w.n_layers

@@ -16,7 +16,8 @@
 //
 // Every weight fragment needs one 1 KiB load and every activation fragment
 // another, so the activation loads per weight byte fall as MF / RF: one
-// fragment per wave suits up to 16 rows, eight per wave 17..64 rows.
+// fragment per wave suits up to 8 rows, two suit 9..16 rows of a wide
+// projection, eight 17..64 rows.
 //
 // Weights come either row-major or packed in the tiled layout of pack.hip,
 // where each 16 x 32 operand block is one contiguous KiB in lane order (one
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
 // Wave arrangements (measured on the tiled layout at 5, 40 and 64 rows and the
 // 8B/70B-share matrix shapes).
 enum SkinnyCfg : int {
-    kCfg1 = 0,     // RF 1, 8 k slices, 4-step buffers: up to 16 rows, and row-major W
+    kCfg1 = 0,     // RF 1, 8 k slices, 4-step buffers: up to 8 rows (16 when N < 8192), and row-major W
     kCfg4 = 1,     // RF 4, 4 k slices, 2-step buffers: 17..64 rows, few output rows
     kCfg8 = 2,     // RF 8, 4 k slices, 1-step buffers: 17..64 rows
     kCfg8R2 = 3,   // RF 8, 2 row groups x 2 k slices: 17..64 rows, very many output rows
@@ -196,8 +197,13 @@ hipError_t launch_shape(const MatmulArgs& a, const uint16_t* act, void* out, int
 template <int MF, int EPI>
 hipError_t launch_mf(const MatmulArgs& a, const uint16_t* act, void* out, int Mc, int ksg,
                      size_t stride, hipStream_t stream) {
-    if constexpr (MF == 1)
+    if constexpr (MF == 1) {
+        // 9..16 rows: every activation load is as large as the weight load
+        // it meets, so wide projections share it between two fragments
+        if (Mc > 8 && a.N >= 8192 && a.tiled)
+            return launch_shape<1, 2, 1, 4, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
         return launch_shape<1, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
+    }
     switch (skinny_cfg(MF, a.N, EPI, a.tiled)) {
         case kCfg1: return launch_shape<MF, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
         case kCfg4:

@@ -54,6 +54,21 @@ def test_small_bf16_forward_rows(M, tiled):
 
 
 @gpu
+@pytest.mark.parametrize("M", [9, 12, 16])
+def test_wide_projections_two_fragments_per_wave(M):
+    """9..16 rows on projections of 8192+ outputs run two weight fragments
+    per wave (up: ffn 8256; head: V 9001 = 563 fragments, so the last
+    workgroup's second fragment is clamped and its outputs skipped)."""
+    sv = require_gpu()
+    w = workload.Workload("wide-bf16", 256, 8256, 2, 9001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 3)
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w, M, sub=M)
+    z = cpu(m.forward(torch.from_numpy(h).cuda()))
+    _check(z, of.forward(model, h), TOL_BF16, f"wide bf16 M={M}")
+
+
+@gpu
 @pytest.mark.parametrize("kind", ["skinny", "tiled"])
 @pytest.mark.parametrize("M", [17, 40, 64, 100])
 def test_bf16_forward_kernel_families(M, kind, monkeypatch):

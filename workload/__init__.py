@@ -33,7 +33,7 @@ __all__ = [
     "Workload", "WORKLOADS", "SWEEP_B", "SWEEP_K", "SWEEP_SIGMA",
     "make_model", "make_hidden", "make_synthetic_logits", "make_random_tokens",
     "KV_BLOCK", "make_paged_attention", "ATTN_WORKLOADS",
-    "MoEWorkload", "MOE_WORKLOADS", "make_moe_model",
+    "MoEWorkload", "MOE_WORKLOADS", "make_moe_model", "make_embedding", "make_start_tokens",
     "bf16_bits_to_f32", "f32_to_bf16_bits",
 ]
 
@@ -87,7 +87,7 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 # Stream ids keep every tensor's draws independent of every other tensor's.
 _STREAM = {"w_up": 1, "w_down": 2, "w_head": 3, "e_head": 4, "hidden": 5,
            "logits_t": 6, "logits_noise": 7, "tokens": 8, "kv": 9, "kv_table": 10,
-           "moe_router": 11, "moe_up": 12, "moe_down": 13}
+           "moe_router": 11, "moe_up": 12, "moe_down": 13, "embed": 14, "start": 15}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -173,6 +173,19 @@ def make_hidden(w: Workload, M: int | None = None, sub: int = 0) -> np.ndarray:
     """Hidden-state inputs [M, d], fp32 N(0, 1)."""
     M = w.M if M is None else M
     return _normal((M, w.d), 1.0, w.seed, _STREAM["hidden"], sub)
+
+
+def make_embedding(w: Workload) -> np.ndarray:
+    """Token embedding table [V, d], fp32 N(0, 1): the input row of a
+    position holding token x is row x (the same law as the hidden-state
+    inputs of the verification workloads)."""
+    return _normal((w.vocab, w.d), 1.0, w.seed, _STREAM["embed"])
+
+
+def make_start_tokens(V: int, B: int, seed: int = 0, sub: int = 0) -> np.ndarray:
+    """B starting tokens, uniform over [0, V), int32."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _STREAM["start"], sub])))
+    return g.integers(0, V, size=B, dtype=np.int32)
 
 
 def make_synthetic_logits(B: int, K: int, V: int, scale: float, sigma: float,

@@ -80,6 +80,16 @@ EXPORTS = {
     "sv_moe_destroy": (None, [_vp]),
     "spec_verify_moe_workspace_bytes": (_sz, [_vp, _i32]),
     "spec_verify_moe_forward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_embed": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "spec_verify_sample_workspace_bytes": (_sz, [_i32, _i32]),
+    "spec_verify_sample": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_float, _u64, _u32, _i32, _vp,
+                                          _i32, _vp, _sz, _vp]),
+    "spec_verify_draft_workspace_bytes": (_sz, [_vp, _i32]),
+    "spec_verify_draft": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _u64, _u32, _vp,
+                                         _vp, _vp, _sz, _vp]),
+    "spec_verify_cycle_workspace_bytes": (_sz, [_vp, _vp, _i32, _i32]),
+    "spec_verify_cycle": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _u64, _u32,
+                                         _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -268,6 +278,98 @@ class Model:
                                       _ptr(out_tokens), _ptr(accept_len), _ptr(p_at), _ptr(q_at),
                                       _ptr(ws), ws.numel(), _stream(stream)))
         return logits, out_tokens, accept_len
+
+
+    def draft_workspace_bytes(self, B: int) -> int:
+        return int(lib().spec_verify_draft_workspace_bytes(self._h, B))
+
+    def draft(self, table, cur, K: int, temperature: float, seed: int, step: int,
+              draft_tokens=None, draft_logits=None, ws=None, stream=None):
+        """The draft loop with this model as the drafter (include/spec_verify_cycle.h):
+        table [V, d] fp32 embedding rows, cur [B] int32 current tokens.
+        Returns (draft_tokens [B, K] int32, draft_logits [B, K, V] fp32)."""
+        B = cur.shape[0]
+        dev = cur.device
+        _need(table, "table", torch.float32, (self.vocab, self.d))
+        _need(cur, "cur", torch.int32, (B,))
+        if draft_tokens is None:
+            draft_tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+        if draft_logits is None:
+            draft_logits = torch.empty((B, K, self.vocab), dtype=torch.float32, device=dev)
+        _need(draft_tokens, "draft_tokens", torch.int32, (B, K))
+        _need(draft_logits, "draft_logits", torch.float32, (B, K, self.vocab))
+        if ws is None:
+            ws = workspace(self.draft_workspace_bytes(B), dev)
+        _check(lib().spec_verify_draft(self._h, _ptr(table), _ptr(cur), B, K, float(temperature),
+                                       int(seed), int(step), _ptr(draft_tokens), _ptr(draft_logits),
+                                       _ptr(ws), ws.numel(), _stream(stream)))
+        return draft_tokens, draft_logits
+
+
+def embed(table, tokens, hidden=None, stream=None):
+    """hidden [n, d] fp32 = table[tokens] (zero rows for tokens outside [0, V))."""
+    V, d = table.shape
+    n = tokens.shape[0]
+    _need(table, "table", torch.float32, (V, d))
+    _need(tokens, "tokens", torch.int32, (n,))
+    if hidden is None:
+        hidden = torch.empty((n, d), dtype=torch.float32, device=table.device)
+    _need(hidden, "hidden", torch.float32, (n, d))
+    _check(lib().spec_verify_embed(_ptr(table), V, d, _ptr(tokens), n, _ptr(hidden), _stream(stream)))
+    return hidden
+
+
+def sample_workspace_bytes(B: int, V: int) -> int:
+    return int(lib().spec_verify_sample_workspace_bytes(B, V))
+
+
+def sample(logits, temperature: float, seed: int, step: int, slot: int, tokens=None,
+           out_stride: int = 1, ws=None, stream=None):
+    """One token per row of logits [B, V]: tokens[b * out_stride] drawn from
+    softmax(logits[b] / T) with Philox counter (b, slot, 2, step)."""
+    B, V = logits.shape
+    _need(logits, "logits", torch.float32, (B, V))
+    if tokens is None:
+        tokens = torch.empty((B * out_stride,), dtype=torch.int32, device=logits.device)
+    _need(tokens, "tokens", torch.int32)
+    if tokens.numel() < (B - 1) * out_stride + 1:
+        raise ValueError("tokens too small for B and out_stride")
+    if ws is None:
+        ws = workspace(sample_workspace_bytes(B, V), logits.device)
+    _check(lib().spec_verify_sample(_ptr(logits), B, V, float(temperature), int(seed), int(step),
+                                    int(slot), _ptr(tokens), int(out_stride), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return tokens
+
+
+def cycle_workspace_bytes(target, drafter, B: int, K: int) -> int:
+    return int(lib().spec_verify_cycle_workspace_bytes(target.handle,
+                                                       drafter.handle if drafter else None, B, K))
+
+
+def cycle(target, drafter, table, cur, K: int, temperature: float, seed: int, step: int,
+          out_tokens=None, accept_len=None, ws=None, stream=None):
+    """One speculative cycle (include/spec_verify_cycle.h): draft K tokens,
+    verify the K + 1 positions, move cur [B] int32 (in place) to the last
+    token emitted.  K = 0 is one step of plain decoding (drafter may be None).
+    Returns (out_tokens [B, K+1], accept_len [B])."""
+    B = cur.shape[0]
+    dev = cur.device
+    _need(table, "table", torch.float32, (target.vocab, target.d))
+    _need(cur, "cur", torch.int32, (B,))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_tokens, "out_tokens", torch.int32, (B, K + 1))
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    if ws is None:
+        ws = workspace(cycle_workspace_bytes(target, drafter, B, K), dev)
+    _check(lib().spec_verify_cycle(target.handle, drafter.handle if drafter else None, _ptr(table),
+                                   _ptr(cur), B, K, float(temperature), int(seed), int(step),
+                                   _ptr(out_tokens), _ptr(accept_len), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+    return out_tokens, accept_len
 
 
 def accept_workspace_bytes(B: int, K: int, V: int) -> int:

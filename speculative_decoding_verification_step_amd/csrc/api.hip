@@ -17,11 +17,8 @@
 
 #include "host.hpp"
 #include "kernels.hpp"
+#include "model.hpp"
 #include "spec_verify.h"
-
-struct sv_model {
-    sv_model_desc desc;
-};
 
 namespace sv {
 
@@ -39,14 +36,11 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
-namespace {
-
 int hip_fail(hipError_t e, const char* what) {
     return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr size_t kAlign = 256;
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+namespace {
 
 // ---- kernel choice ---------------------------------------------------------
 // bf16 weights: matrix cores with the weights streamed straight to registers
@@ -111,6 +105,10 @@ ForwardPlan plan_forward(const sv_model_desc& d, int M) {
     p.bytes = off;
     return p;
 }
+
+}  // namespace
+
+size_t forward_bytes(const sv_model_desc& d, int M) { return plan_forward(d, M).bytes; }
 
 // Per-chunk softmax statistics: (max, sum) for every target and draft row,
 // argmax for every target row.
@@ -199,6 +197,8 @@ int run_accept(const float* tl, const float* dl, const int32_t* x, int B, int K,
     if (e != hipSuccess) return hip_fail(e, "accept launch");
     return SV_OK;
 }
+
+namespace {
 
 int check_accept_args(const float* tl, const float* dl, const int32_t* x, int B, int K, int V,
                       float T, const int32_t* out, const int32_t* al) {

@@ -87,7 +87,7 @@ int skinny_splits(int M, int N, int K, int tiled);
 int stats_chunks(int V);
 hipError_t launch_row_stats(const float* target, const float* draft, int n_t, int n_d, int V,
                             float inv_t, int greedy, float* pv, float* ps, int* pi,
-                            hipStream_t stream);
+                            hipStream_t stream, float* copy = nullptr, size_t copy_stride = 0);
 
 // Accept / resample / bonus for B requests, folding the chunk statistics
 // written by launch_row_stats.  `scratch` holds accept_meta_floats(B, V)
@@ -97,6 +97,17 @@ hipError_t launch_accept(const float* target, const float* draft, const int32_t*
                          int K, int V, float inv_t, int greedy, uint64_t seed, uint32_t step,
                          const float* pv, const float* ps, const int* pi, float* scratch,
                          int32_t* out_tokens, int32_t* accept_len, float* p_at, float* q_at,
+                         hipStream_t stream);
+
+// One token per row of logits [B, V]: the bonus-token draw of a verification
+// with no draft positions (inverse CDF of softmax(z / T) in ascending ids;
+// argmax, lowest id on ties, at T = 0), its uniform from Philox counter
+// (b, slot, 2, step).  Token b goes to tokens[b * out_stride].  pv/ps/pi are
+// launch_row_stats' statistics of the B rows; scratch holds
+// accept_meta_floats(B, V) floats.
+hipError_t launch_sample(const float* logits, int B, int V, float inv_t, int greedy,
+                         uint64_t seed, uint32_t step, int slot, const float* pv, const float* ps,
+                         const int* pi, float* scratch, int32_t* tokens, int out_stride,
                          hipStream_t stream);
 
 // Per-launch timing hook (implemented by the host layer).  When profiling is

@@ -87,10 +87,12 @@ __device__ __forceinline__ void arg_merge(float& v, int& i, float v2, int i2) {
     }
 }
 
+// `copy` (optional): the target rows are also written to copy + row *
+// copy_stride (a row of a larger array), from the registers they were read into.
 __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, int n_t, int V,
     int nchunk, float inv_t, int greedy, int vec4, float* __restrict__ pv,
-    float* __restrict__ ps, int* __restrict__ pi) {
+    float* __restrict__ ps, int* __restrict__ pi, float* __restrict__ copy, size_t copy_stride) {
     const int row = blockIdx.x / nchunk;
     const int chunk = blockIdx.x - row * nchunk;
     const int tid = threadIdx.x;
@@ -119,6 +121,15 @@ __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[4 * v + i] = (e + i < V) ? z[e + i] : -INFINITY;
         }
+    }
+
+    if (copy && row < n_t) {
+        float* dst = copy + (size_t)row * copy_stride;
+#pragma unroll
+        for (int v = 0; v < kPerThread / 4; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (idx0[v] + i < V) dst[idx0[v] + i] = x[4 * v + i];
     }
 
     __shared__ float sh_v[kStatsThreads / kWave];
@@ -335,8 +346,8 @@ __device__ int decide(const float* target, const float* draft, const int32_t* to
 
 __device__ __forceinline__ void write_outputs(int32_t* out, int32_t* accept_len,
                                               const int32_t* tokens, int b, int K, int js,
-                                              int tok) {
-    int32_t* ob = out + (size_t)b * (K + 1);
+                                              int tok, int out_stride) {
+    int32_t* ob = out + (size_t)b * out_stride;
     for (int y = threadIdx.x; y <= K; y += kDrawThreads) {
         int32_t v = -1;
         if (js > 0) {
@@ -345,7 +356,7 @@ __device__ __forceinline__ void write_outputs(int32_t* out, int32_t* accept_len,
         }
         ob[y] = v;
     }
-    if (threadIdx.x == 0) accept_len[b] = js > 0 ? js : 0;
+    if (threadIdx.x == 0 && accept_len) accept_len[b] = js > 0 ? js : 0;
 }
 
 __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
     uint32_t k0, uint32_t k1, uint32_t step, const float* __restrict__ pv,
     const float* __restrict__ ps, const int* __restrict__ pi, float* __restrict__ ctot,
     float* __restrict__ meta, int32_t* __restrict__ out, int32_t* __restrict__ accept_len,
-    float* __restrict__ p_at, float* __restrict__ q_at, int B) {
+    float* __restrict__ p_at, float* __restrict__ q_at, int B, int out_stride) {
     const int b = blockIdx.x / nchunk;
     const int c = blockIdx.x - b * nchunk;
     __shared__ int sh_first, sh_bad;
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
         // nothing to draw: the first chunk's workgroup writes the request
         if (c == 0) {
             const int tok = js < 0 ? -1 : wave_row_argmax(pv, pi, (size_t)b * (K + 1) + js - 1, nchunk);
-            write_outputs(out, accept_len, tokens, b, K, js, tok);
+            write_outputs(out, accept_len, tokens, b, K, js, tok, out_stride);
             if (threadIdx.x == 0) meta[(size_t)b * kMeta] = __int_as_float(0);
         }
         return;
@@ -432,11 +443,15 @@ __device__ int find_in_chunk(const DrawRows& dr, int c, int V, float prefix, flo
     return r == INT_MAX ? -1 : r;
 }
 
+// The draw's uniform is word 0 of Philox at counter (b, js + pos_base,
+// draw_id, step): (b, js, 1, step) for the replacement or bonus token of a
+// verification, (b, slot, 2, step) for a token drawn from a draft row.
 __global__ __launch_bounds__(kDrawThreads) void draw_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, int K, int V, int nchunk, float inv_t, uint32_t k0,
-    uint32_t k1, uint32_t step, const float* __restrict__ ctot, const float* __restrict__ meta,
-    int32_t* __restrict__ out, int32_t* __restrict__ accept_len) {
+    uint32_t k1, uint32_t step, uint32_t draw_id, int pos_base, const float* __restrict__ ctot,
+    const float* __restrict__ meta, int32_t* __restrict__ out, int32_t* __restrict__ accept_len,
+    int out_stride) {
     const int b = blockIdx.x;
     const float* mb = meta + (size_t)b * kMeta;
     const int js = __float_as_int(mb[0]);
@@ -453,7 +468,8 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(
     dr.md = mb[3];
     dr.id_s = mb[4];
     dr.inv_t = inv_t;
-    const float u = u_resample(philox_word0((uint32_t)b, (uint32_t)js, 1u, step, k0, k1));
+    const float u =
+        u_resample(philox_word0((uint32_t)b, (uint32_t)(js + pos_base), draw_id, step, k0, k1));
     const float* ct = ctot + (size_t)b * nchunk;
 
     // R, the threshold and its chunk (thread 0, chunk order).  R == 0 after a
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(
         __syncthreads();
         tok = sh_i[1] < 0 ? 0 : sh_i[1];
     }
-    write_outputs(out, accept_len, tokens, b, K, js, tok);
+    write_outputs(out, accept_len, tokens, b, K, js, tok, out_stride);
 }
 
 }  // namespace
@@ -529,15 +545,16 @@ size_t accept_meta_floats(int B, int V) { return (size_t)B * stats_chunks(V) + (
 
 hipError_t launch_row_stats(const float* target, const float* draft, int n_t, int n_d, int V,
                             float inv_t, int greedy, float* pv, float* ps, int* pi,
-                            hipStream_t stream) {
+                            hipStream_t stream, float* copy, size_t copy_stride) {
     const int rows = n_t + n_d;
     if (rows <= 0) return hipSuccess;
     const int nchunk = stats_chunks(V);
     const int vec4 = (V % 4 == 0) && ((uintptr_t)target % 16 == 0) &&
                      (draft == nullptr || (uintptr_t)draft % 16 == 0);
-    ProfScope prof("row_stats", stream, (double)rows * V * 4.0, 0.0);
+    const double copied = copy ? (double)n_t * V * 4.0 : 0.0;
+    ProfScope prof("row_stats", stream, (double)rows * V * 4.0 + copied, 0.0);
     SV_LAUNCH(prof, row_stats_kernel, rows * nchunk, kStatsThreads, stream, target, draft, n_t, V,
-              nchunk, inv_t, greedy, vec4, pv, ps, pi);
+              nchunk, inv_t, greedy, vec4, pv, ps, pi, copy, copy_stride);
     return hipGetLastError();
 }
 
@@ -556,14 +573,41 @@ hipError_t launch_accept(const float* target, const float* draft, const int32_t*
         ProfScope prof("decide_chunk", stream, greedy ? 0.0 : (double)B * 2.0 * V * 4.0, 0.0);
         SV_LAUNCH(prof, decide_chunk_kernel, B * nchunk, kDrawThreads, stream, target, draft,
                   tokens, K, V, nchunk, inv_t, greedy, k0, k1, step, pv, ps, pi, ctot, meta,
-                  out_tokens, accept_len, p_at, q_at, B);
+                  out_tokens, accept_len, p_at, q_at, B, K + 1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (greedy) return hipSuccess;
     ProfScope prof("draw", stream, (double)B * 2.0 * kChunk * 4.0, 0.0);
     SV_LAUNCH(prof, draw_kernel, B, kDrawThreads, stream, target, draft, tokens, K, V, nchunk,
-              inv_t, k0, k1, step, ctot, meta, out_tokens, accept_len);
+              inv_t, k0, k1, step, 1u, 0, ctot, meta, out_tokens, accept_len, K + 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_sample(const float* logits, int B, int V, float inv_t, int greedy,
+                         uint64_t seed, uint32_t step, int slot, const float* pv, const float* ps,
+                         const int* pi, float* scratch, int32_t* tokens, int out_stride,
+                         hipStream_t stream) {
+    if (B <= 0) return hipSuccess;
+    const int nchunk = stats_chunks(V);
+    const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
+    float* ctot = scratch;
+    float* meta = scratch + (size_t)B * nchunk;
+    // a verification with no draft positions: every row is a bonus row
+    {
+        ProfScope prof("decide_chunk", stream, greedy ? 0.0 : (double)B * V * 4.0, 0.0);
+        SV_LAUNCH(prof, decide_chunk_kernel, B * nchunk, kDrawThreads, stream, logits,
+                  (const float*)nullptr, (const int32_t*)nullptr, 0, V, nchunk, inv_t, greedy, k0,
+                  k1, step, pv, ps, pi, ctot, meta, tokens, (int32_t*)nullptr, (float*)nullptr,
+                  (float*)nullptr, B, out_stride);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (greedy) return hipSuccess;
+    ProfScope prof("draw", stream, (double)B * kChunk * 4.0, 0.0);
+    SV_LAUNCH(prof, draw_kernel, B, kDrawThreads, stream, logits, (const float*)nullptr,
+              (const int32_t*)nullptr, 0, V, nchunk, inv_t, k0, k1, step, 2u, slot - 1, ctot, meta,
+              tokens, (int32_t*)nullptr, out_stride);
     return hipGetLastError();
 }
 

@@ -178,3 +178,61 @@ def test_packed_sizes_and_pack_rejects(L):
     assert pw(FAKE, FAKE + 8, 16, 64, 1, None) == bd.SV_ERR_INVALID_ARG     # misaligned
     assert pw(FAKE, FAKE + 512, 16, 64, 1, None) == bd.SV_ERR_INVALID_ARG   # overlap
     assert pw(FAKE, FAKE, 16, 64, 0, None) == 0                             # nothing to do
+
+
+def test_cycle_entry_points_reject(L):
+    """The draft loop, the sampler, the embedding gather and the cycle check
+    every argument on the host (include/spec_verify_cycle.h)."""
+    rc, tgt = _create(L)
+    rc2, drf = _create(L, n_layers=1)
+    rc3, odd = _create(L, d=512)
+    assert rc == rc2 == rc3 == 0
+    try:
+        em = L.spec_verify_embed
+        assert em(FAKE, 0, 256, FAKE, 3, FAKE, None) == bd.SV_ERR_INVALID_ARG
+        assert em(FAKE, 4096, 6, FAKE, 3, FAKE, None) == bd.SV_ERR_INVALID_ARG
+        assert em(FAKE + 4, 4096, 256, FAKE, 3, FAKE, None) == bd.SV_ERR_INVALID_ARG
+        assert em(0, 4096, 256, FAKE, 3, FAKE, None) == bd.SV_ERR_INVALID_ARG
+        assert em(0, 4096, 256, 0, 0, 0, None) == 0                        # n = 0: nothing to do
+
+        sm = L.spec_verify_sample
+        need = L.spec_verify_sample_workspace_bytes(4, 4096)
+        assert need > 0
+        assert sm(FAKE, 4, 4096, 1.0, 0, 0, 0, FAKE, 1, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert sm(FAKE, 4, 4096, 1.0, 0, 0, 1, FAKE, 0, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert sm(FAKE, 4, 4096, -1.0, 0, 0, 1, FAKE, 1, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert sm(FAKE, 4, 4096, 1.0, 0, 0, 1, FAKE, 1, FAKE, need - 1, None) == bd.SV_ERR_WORKSPACE
+        assert sm(0, 4, 4096, 1.0, 0, 0, 1, FAKE, 1, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert sm(0, 0, 4096, 1.0, 0, 0, 1, 0, 1, 0, 0, None) == 0            # B = 0
+
+        dr = L.spec_verify_draft
+        need = L.spec_verify_draft_workspace_bytes(drf, 2)
+        assert need > L.spec_verify_forward_workspace_bytes(drf, 2)
+        assert dr(None, FAKE, FAKE, 2, 3, 1.0, 0, 0, FAKE, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert dr(drf, 0, FAKE, 2, 3, 1.0, 0, 0, FAKE, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert dr(drf, FAKE, FAKE, 2, -1, 1.0, 0, 0, FAKE, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert dr(drf, FAKE, FAKE, 2, 3, 1.0, 0, 0, 0, FAKE, FAKE, need, None) == bd.SV_ERR_INVALID_ARG
+        assert dr(drf, FAKE, FAKE, 2, 3, 1.0, 0, 0, FAKE, FAKE, FAKE, need - 1, None) == bd.SV_ERR_WORKSPACE
+        assert dr(drf, FAKE, FAKE, 2, 0, 1.0, 0, 0, 0, 0, 0, 0, None) == 0   # K = 0: nothing to draft
+
+        cy = L.spec_verify_cycle
+        need = L.spec_verify_cycle_workspace_bytes(tgt, drf, 2, 3)
+        assert need > L.spec_verify_workspace_bytes(tgt, 2, 3)
+        assert L.spec_verify_cycle_workspace_bytes(tgt, None, 2, 3) == 0     # K > 0 needs a drafter
+        assert L.spec_verify_cycle_workspace_bytes(tgt, None, 2, 0) > 0
+        args = lambda **k: dict(dict(t=tgt, d=drf, tab=FAKE, cur=FAKE, B=2, K=3, T=1.0, out=FAKE,
+                                     al=FAKE, ws=FAKE, n=need), **k)
+        run = lambda a: cy(a["t"], a["d"], a["tab"], a["cur"], a["B"], a["K"], a["T"], 0, 0,
+                           a["out"], a["al"], a["ws"], a["n"], None)
+        assert run(args(t=None)) == bd.SV_ERR_INVALID_ARG
+        assert run(args(d=None)) == bd.SV_ERR_INVALID_ARG
+        assert run(args(d=odd)) == bd.SV_ERR_INVALID_ARG                     # d differs
+        assert run(args(T=float("inf"))) == bd.SV_ERR_INVALID_ARG
+        assert run(args(cur=0)) == bd.SV_ERR_INVALID_ARG
+        assert run(args(out=0)) == bd.SV_ERR_INVALID_ARG
+        assert run(args(n=need - 1)) == bd.SV_ERR_WORKSPACE
+        assert run(args(K=-1)) == bd.SV_ERR_INVALID_ARG
+        assert run(args(B=0, out=0, al=0, ws=0, n=0)) == 0
+    finally:
+        for h in (tgt, drf, odd):
+            L.sv_model_destroy(h)

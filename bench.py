@@ -18,7 +18,11 @@ Prints ONE JSON line.  Default workload: the 8B-shaped stack at B=1, K=4
 8B-shaped stack (B in 1,4,16,64; K in 1,2,4,8).  ``--crossover`` prints the
 forward-only time of each MFMA kernel family (weights streamed to registers
 vs LDS-staged GEMM) per row count, to locate the HBM -> MFMA crossover in
-B*(K+1).
+B*(K+1).  ``--k-table`` measures T_verif(M) and AL(K) and prints the
+goodput-optimal draft length per batch size; ``--attention`` times the paged
+attention of the verified positions; ``--moe`` sweeps the mixture-of-experts
+target over B x K; ``--cycle`` times whole speculative cycles (draft loop +
+verification) against plain decoding.
 """
 from __future__ import annotations
 
@@ -455,7 +459,6 @@ def _moe_bench(a):
     acceptance lengths (Cohere DSD: for MoE the optimum need not fall with B)."""
     import torch
     import speculative_decoding_verification_step_amd as sv
-    from oracle import moe as om
     w = workload.MOE_WORKLOADS["moe-64e-top6-b1-k4"]
     T = 1.0
     for sigma in workload.SWEEP_SIGMA:
@@ -507,7 +510,8 @@ def _moe_bench(a):
                 times.setdefault(M, []).append(ms)
                 rec = {"moe": w.name, "sigma": sigma, "B": B, "K": K, "M": M, "ms_per_step": ms,
                        "active_experts_per_block": act,
-                       "expected_active_uniform": om.expected_active(E, w.top_k, M),
+                       # distinct experts if every position picked top_k of E uniformly
+                       "expected_active_uniform": E * (1.0 - (1.0 - w.top_k / E) ** M),
                        "step_bytes": bytes_, "step_hbm_frac": bytes_ / (ms / 1e3) / (HBM_PEAK_GBS * 1e9),
                        "verified_positions_per_s": M / (ms / 1e3),
                        "launch": "hipgraph" if a.graph else "eager"}
@@ -599,6 +603,87 @@ def _attention_bench(a):
             torch.cuda.empty_cache()
 
 
+CYCLE_B = (1, 4, 16, 64)
+CYCLE_K = tuple(range(7))      # K = 0: plain decoding
+CYCLE_EXITS = (0, 1)           # drafter = the target's first n blocks, final norm and head
+CYCLE_STATS = 32               # cycles per point for the acceptance statistics
+
+
+def _cycle_bench(a):
+    """Whole speculative cycles on the 8B-shaped target (publishertech
+    section 2, "Theoretical Speedup Equation"): the drafter is an early exit
+    of the target (its first n blocks, its final norm and head; no weights of
+    its own), tokens feed back through an embedding table, and one cycle is
+    the draft loop, the verification of the K + 1 positions and the next
+    input token, all on the device.  Per drafter, B and K: ms per cycle
+    (eager, and one captured graph replayed), emitted tokens per second,
+    the measured acceptance rate alpha and draft cost c (one draft step over
+    one plain decoding step), and the speedup over plain decoding (K = 0)
+    beside the pages' model E[N] / (1 + K c) with E[N] = (1 - alpha^(K+1)) /
+    (1 - alpha)."""
+    import torch
+    import speculative_decoding_verification_step_amd as sv
+    w = workload.WORKLOADS["8b-shaped-b1-k4"]
+    T = 1.0 if a.T is None else a.T
+    target, _, _ = _device_models(w, w.sigma)
+    up, down, gain, head = target._keep
+    table = torch.from_numpy(workload.make_embedding(w)).cuda()
+    d, ffn, V = w.d, w.ffn, w.vocab
+    for n_exit in CYCLE_EXITS:
+        g_d = torch.cat([gain[:n_exit], gain[-1:]]).contiguous()
+        drafter = sv.Model(up, down, g_d, head, layout="tiled", dims=(n_exit, d, ffn, V))
+        for B in CYCLE_B:
+            start = torch.from_numpy(workload.make_start_tokens(V, B, seed=B)).cuda()
+            cur = start.clone()
+            dws = sv.workspace(drafter.draft_workspace_bytes(B))
+            dtok = torch.empty((B, 1), dtype=torch.int32, device="cuda")
+            dlog = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
+            t_draft = _time_fn(lambda s: drafter.draft(table, cur, 1, T, 1, 0, dtok, dlog, dws, s),
+                               20, 2, False)
+            rows = []
+            for K in CYCLE_K:
+                dr = drafter if K else None
+                ws = sv.workspace(sv.cycle_workspace_bytes(target, dr, B, K))
+                out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+                al = torch.empty((B,), dtype=torch.int32, device="cuda")
+                cur = start.clone()
+                als = []
+                for stp in range(CYCLE_STATS):
+                    sv.cycle(target, dr, table, cur, K, T, 7, stp, out, al, ws)
+                    als.append(al.clone())
+                al_all = torch.stack(als).cpu().numpy()
+                cur = start.clone()
+
+                def one(s):
+                    sv.cycle(target, dr, table, cur, K, T, 7, 0, out, al, ws, stream=s)
+                ms = _time_fn(one, 20, 2, False)
+                ms_graph = _time_fn(one, 20, 2, True)
+                mean_al = float(al_all.mean())
+                alpha = float((al_all - 1).sum() / np.minimum(al_all, K).sum()) if K else None
+                rows.append({"K": K, "ms_per_cycle": ms, "graph_ms_per_cycle": ms_graph,
+                             "mean_accept_len": mean_al, "alpha": alpha,
+                             "tokens_per_s": B * mean_al / (ms / 1e3)})
+                del ws, out, al
+            t0 = rows[0]["ms_per_cycle"]
+            c = t_draft / t0
+            for r in rows:
+                K, alpha = r["K"], r["alpha"]
+                en = 1.0 if K == 0 else ((1 - alpha ** (K + 1)) / (1 - alpha) if alpha < 1 else K + 1.0)
+                rec = {"cycle": w.name, "drafter": f"exit-{n_exit}", "B": B, "T": T, **r,
+                       "draft_step_ms": t_draft, "c": c,
+                       "speedup_measured": r["tokens_per_s"] / rows[0]["tokens_per_s"],
+                       "speedup_model": en / (1 + K * c),
+                       "launch": "eager (graph replay beside it)"}
+                print(json.dumps(rec), flush=True)
+            best = max(rows, key=lambda r: r["tokens_per_s"])
+            print(json.dumps({"cycle_best": w.name, "drafter": f"exit-{n_exit}", "B": B, "K": best["K"],
+                              "speedup": best["tokens_per_s"] / rows[0]["tokens_per_s"], "c": c}),
+                  flush=True)
+            del dws, dtok, dlog
+        del drafter
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -627,6 +712,9 @@ def main():
                          "goodput-optimal draft length per batch size")
     ap.add_argument("--crossover", action="store_true",
                     help="forward-only times of both MFMA kernel families over B*(K+1)")
+    ap.add_argument("--cycle", action="store_true",
+                    help="whole speculative cycles (draft loop + verification) with early-exit "
+                         "drafters: tokens/s, acceptance, draft cost and speedup over plain decoding")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with one plain 256 MiB device copy (counter calibration)")
     a = ap.parse_args()
@@ -658,6 +746,9 @@ def main():
         return
     if a.moe:
         _moe_bench(a)
+        return
+    if a.cycle:
+        _cycle_bench(a)
         return
     if a.crossover:
         # forward-only time per row count with each MFMA family forced: the

@@ -19,12 +19,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// Round fp32 to bf16, nearest-even; NaN stays NaN.
+// Round fp32 to bf16, nearest-even; NaN stays NaN (quiet).  Branch-free (a
+// select), so a loop that converts its operands keeps its loads in flight.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t b = __float_as_uint(f);
-    if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x7fffffu)) return (b >> 16) | 0x40u;
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return b >> 16;
+    const uint32_t b = __float_as_uint(f);
+    const uint32_t rne = (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+    return (b & 0x7fffffffu) > 0x7f800000u ? ((b >> 16) | 0x40u) : rne;
 }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }

@@ -58,20 +58,26 @@ int forced_kind() {
     return k;
 }
 
-// From this many rows the weights are reused from LDS (kMfmaTiled); below it
-// every weight is streamed once in a single pass (kMfmaSkinny, up to 64
-// rows).  Measured on the 8B-shaped stack: one streaming pass wins at 64 rows
-// (0.67 vs 0.90 ms per forward), the LDS-staged GEMM beats two passes from 80
-// rows on (0.91 vs 1.17 ms).
-constexpr int kTiledMinRows = 65;
+// From kTiledMinRows rows the weights are reused from LDS (kMfmaTiled); below
+// it every weight is streamed once per pass of up to 128 rows (kMfmaSkinny).
+// From kActTiledMinRows rows the streaming kernel reads its activations in
+// the operand layout (one contiguous KiB per 16 rows x 32 k) instead of
+// row-major (16 rows x 64 bytes at a row stride): measured on the 8B-shaped
+// stack, 0.478 vs 0.520 ms per forward at 17 rows and 0.553 vs 0.660 at 64.
+// Below it row-major wins, since rows past M cost nothing there.
+constexpr int kTiledMinRows = 129;
+constexpr int kActTiledMinRows = 17;
+// The LM head moves to the LDS-staged GEMM earlier: 65+ rows (measured on the
+// 8B-shaped head at 96 and 128 rows: 64 and 66 us vs 79 and 79 us streamed).
+constexpr int kHeadTiledMinRows = 65;
 
-int matmul_kind(const sv_model_desc& d, int M) {
+int matmul_kind(const sv_model_desc& d, int M, bool head = false) {
     if (d.wdtype != SV_BF16) return kGemvValu;
     if (d.layout == SV_LAYOUT_TILED) {
         const char* e = getenv("SPEC_VERIFY_MATMUL");
         if (e && !strcmp(e, "skinny")) return kMfmaSkinny;
         if (e && !strcmp(e, "tiled")) return kMfmaTiled;
-        return M >= kTiledMinRows ? kMfmaTiled : kMfmaSkinny;
+        return M >= (head ? kHeadTiledMinRows : kTiledMinRows) ? kMfmaTiled : kMfmaSkinny;
     }
     const int f = forced_kind();
     if (f >= 0) return f;
@@ -80,9 +86,11 @@ int matmul_kind(const sv_model_desc& d, int M) {
 
 struct ForwardPlan {
     int M = 0;
-    int kind = kGemvValu;
+    int kind = kGemvValu;    // up and down projections
+    int head_kind = kGemvValu;
     int splits = 0;          // K splits (partial planes) of the down projection
-    int act_tiled = 0;       // bf16 activations in the operand layout (LDS-staged GEMM)
+    int act_tiled = 0;       // bf16 activations in the operand layout (LDS-staged GEMM,
+                             // and the streaming kernel from kActTiledMinRows rows)
     size_t off_h = 0, off_a = 0, off_s = 0, off_part = 0, bytes = 0;
 };
 
@@ -90,11 +98,12 @@ ForwardPlan plan_forward(const sv_model_desc& d, int M) {
     ForwardPlan p;
     p.M = M;
     p.kind = matmul_kind(d, M);
+    p.head_kind = matmul_kind(d, M, true);
     const int tiled = d.layout == SV_LAYOUT_TILED;
+    p.act_tiled = p.kind == kMfmaTiled || (p.kind == kMfmaSkinny && tiled && M >= kActTiledMinRows);
     p.splits = p.kind == kMfmaTiled    ? tiled_splits(M, d.d, d.ffn)
-               : p.kind == kMfmaSkinny ? skinny_splits(M, d.d, d.ffn, tiled)
+               : p.kind == kMfmaSkinny ? skinny_splits(M, d.d, d.ffn, tiled, p.act_tiled)
                                        : 0;
-    p.act_tiled = p.kind == kMfmaTiled;
     const int es = d.wdtype == SV_BF16 ? 2 : 4;
     const size_t arows = p.act_tiled ? (size_t)(M + 15) / 16 * 16 : (size_t)M;
     size_t off = 0;
@@ -171,7 +180,7 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
     hd.M = M; hd.N = d.vocab; hd.K = d.d;
     hd.epi = kEpiStore; hd.out = logits; hd.bf16 = bf16; hd.tiled = tiled;
     hd.act_tiled = p.act_tiled;
-    e = launch_matmul(hd, p.kind, s);
+    e = launch_matmul(hd, p.head_kind, s);
     if (e != hipSuccess) return hip_fail(e, "LM-head launch");
     return SV_OK;
 }

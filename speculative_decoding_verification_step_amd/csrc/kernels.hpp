@@ -26,7 +26,8 @@ struct MatmulArgs {
     int bf16;             // 1: bf16 weights/activations, 0: fp32
     int tiled;            // 1: W in the MFMA-tiled layout of pack.hip (bf16 only)
     int act_tiled;        // 1: `act` (and the kEpiSilu output) in the operand layout of
-                          // the tiled weights, rows padded to 16 (kMfmaTiled only)
+                          // the tiled weights, rows padded to 16 (MFMA kernels,
+                          // tiled weights only)
     int splits;           // kEpiResidual on the MFMA kernels: K split count (0 = add
                           // into h); `out` then holds `splits` fp32 partial
                           // planes [M, N] that the next RMSNorm folds in
@@ -78,7 +79,7 @@ hipError_t launch_rmsnorm_moe(float* h, const MoeFold& fold, const float* gain, 
 // (so that the tile grid fills the chip).
 int tiled_splits(int M, int N, int K);
 // Split count of the streaming MFMA kernel's down projection (0: no split).
-int skinny_splits(int M, int N, int K, int tiled);
+int skinny_splits(int M, int N, int K, int tiled, int act_tiled);
 
 // Softmax statistics at temperature T (1/T = inv_t), per chunk of
 // stats_chunks(V) chunks of each row: chunk max and sum of exp((z - max) / T)

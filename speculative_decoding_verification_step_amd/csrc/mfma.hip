@@ -1,5 +1,5 @@
 // bf16 MFMA matmuls out[m, n] = sum_k act[m, k] * W[n, k] on gfx950 matrix
-// cores, for the verification forward at B*(K+1) = 1..64 rows per pass.
+// cores, for the verification forward at B*(K+1) = 1..128 rows per pass.
 //
 // The weights are the stream (read once, publishertech section 1 "The
 // Speculative Cycle"); the activations are small and stay in L1/L2.  A wave
@@ -17,7 +17,9 @@
 // Every weight fragment needs one 1 KiB load and every activation fragment
 // another, so the activation loads per weight byte fall as MF / RF: one
 // fragment per wave suits up to 8 rows, two suit 9..16 rows of a wide
-// projection, eight 17..64 rows.
+// projection, four or eight 17..128 rows.  Up to 16 rows the activations are
+// row-major (rows past M cost nothing); from 17 rows they come in the
+// operand layout, where each activation load is one contiguous KiB.
 //
 // Weights come either row-major or packed in the tiled layout of pack.hip,
 // where each 16 x 32 operand block is one contiguous KiB in lane order (one
@@ -31,7 +33,7 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-template <int MF, int RF, int NR, int NKS, int U, int EPI, bool kTiled>
+template <int MF, int RF, int NR, int NKS, int U, int EPI, bool kTiled, bool kActT>
 __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ act, int M, int N, int K,
     int steps_per_split, void* __restrict__ out, size_t split_stride) {
@@ -51,29 +53,35 @@ __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
     const int len = max(min(S, gs0 + steps_per_split) - gs0, 0);
     const int s0 = gs0 + (int)((long long)len * ks / NKS);
     const int s1 = gs0 + (int)((long long)len * (ks + 1) / NKS);
-    const int fb0 = (blockIdx.x * NR + rg) * RF;
+    const int fb0 = __builtin_amdgcn_readfirstlane((blockIdx.x * NR + rg) * RF);
 
-    // weight operand of step s for fragment rf: wrow[rf] + wstep * s
-    const uint16_t* wrow[RF];
-    constexpr int wstep = kTiled ? 512 : 32;
+    // weight operand of step s for fragment rf.  Tiled: the wave's fragments
+    // are contiguous (S KiB each) from the wave-uniform base wbase, so a load
+    // needs only a 32-bit lane offset; fragments past N read as zeros.
+    // Row-major (one fragment): wrow + 32 * s, this lane's row.
+    const char* wbase = reinterpret_cast<const char*>(W + (size_t)fb0 * S * 512);
+    bool wval[RF];
 #pragma unroll
-    for (int rf = 0; rf < RF; ++rf) {
-        const int fb = min(fb0 + rf, nblk - 1);
-        if constexpr (kTiled) {
-            wrow[rf] = W + (size_t)fb * S * 512 + lane * 8;
-        } else {
-            const int n = min(fb * 16 + r16, N - 1);
-            wrow[rf] = W + (size_t)n * K + 8 * g;
-        }
-    }
-    const uint16_t* arow[MF];
+    for (int rf = 0; rf < RF; ++rf) wval[rf] = fb0 + rf < nblk;
+    const uint16_t* wrow = W + (size_t)min(fb0 * 16 + r16, N - 1) * K + 8 * g;
+    // activation operand of step s for fragment mf.  Row-major: arow[mf] +
+    // 32 * s, this lane's row; rows past M read as zeros.  Operand layout: the
+    // KiB of row block mf at step s lies (mf * S + s) KiB into the pass (the
+    // pass base and a 32-bit lane offset); its rows past M are padding whose
+    // outputs are dropped.
+    const uint16_t* arow[kActT ? 1 : MF];
     bool aval[MF];
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
-        const int m = mf * 16 + r16;
-        aval[mf] = m < M;
-        arow[mf] = act + (size_t)min(m, M - 1) * K + 8 * g;
+        if constexpr (kActT) {
+            aval[mf] = mf * 16 < M;
+        } else {
+            const int m = mf * 16 + r16;
+            aval[mf] = m < M;
+            arow[mf] = act + (size_t)min(m, M - 1) * K + 8 * g;
+        }
     }
+    const char* abase = reinterpret_cast<const char*>(act);
 
     f32x4v acc[RF][MF];
 #pragma unroll
@@ -89,15 +97,20 @@ __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
         for (int u = 0; u < U; ++u) {
             const int ss = s + u;
             const bool in = ss < s1;
-            const int k = 32 * ss;
 #pragma unroll
             for (int mf = 0; mf < MF; ++mf)
-                x[u][mf] = (in && aval[mf]) ? *reinterpret_cast<const bf16x8*>(arow[mf] + k) : zero8;
+                x[u][mf] = (in && aval[mf])
+                               ? *reinterpret_cast<const bf16x8*>(
+                                     kActT ? abase + (uint32_t)(lane * 16 + (mf * S + ss) * 1024)
+                                           : reinterpret_cast<const char*>(arow[mf] + 32 * ss))
+                               : zero8;
 #pragma unroll
             for (int rf = 0; rf < RF; ++rf)
-                w[u][rf] = in ? __builtin_nontemporal_load(
-                                    reinterpret_cast<const bf16x8*>(wrow[rf] + (size_t)wstep * ss))
-                              : zero8;
+                w[u][rf] = (in && wval[rf])
+                               ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(
+                                     kTiled ? wbase + (uint32_t)(lane * 16 + (rf * S + ss) * 1024)
+                                            : reinterpret_cast<const char*>(wrow + 32 * ss)))
+                               : zero8;
         }
     };
     auto compute = [&](const bf16x8 (&w)[U][RF], const bf16x8 (&x)[U][MF]) {
@@ -120,38 +133,66 @@ __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
     }
 
     // fixed-order reduction of the NKS k slices through LDS, one weight
-    // fragment of every row group at a time
-    __shared__ float red[NKS][NR][MF][4][kWave];
+    // fragment of every row group at a time.  Each wave stores its
+    // accumulators lane-major (one 16-byte write per lane and fragment); each
+    // task then sums the NKS copies of one lane's four outputs (16-byte
+    // reads, no bank conflicts) and writes four consecutive outputs n0..n0+3
+    // of one row m: the lane's rows of the MFMA result tile.
+    __shared__ f32x4v red[NKS][NR][MF][kWave];
     float* plane = static_cast<float*>(out) + (size_t)blockIdx.y * split_stride;
+    // rows start 16-byte aligned (8 for bf16 outputs)
+    const bool vec = (N & 3) == 0 && ((uintptr_t)out & (EPI == kEpiSilu ? 7 : 15)) == 0;
 #pragma unroll
     for (int rf = 0; rf < RF; ++rf) {
         if (rf) __syncthreads();        // the previous fragment's readers are done
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[ks][rg][mf][r][lane] = acc[rf][mf][r];
+        for (int mf = 0; mf < MF; ++mf) red[ks][rg][mf][lane] = acc[rf][mf];
         __syncthreads();
-        constexpr int kOut = 256 * MF * NR;
-        for (int e = threadIdx.x; e < kOut; e += NWK * kWave) {
-            const int i = e & 15;                 // row within the 16-row fragment
-            const int j = (e >> 4) & 15;          // column (position) within the fragment
-            const int mf = (e >> 8) % MF;
-            const int rr = (e >> 8) / MF;
-            const int n = ((blockIdx.x * NR + rr) * RF + rf) * 16 + i;
-            const int m = mf * 16 + j;
-            if (n >= N || m >= M) continue;
-            const int r = i & 3, l = ((i >> 2) << 4) + j;
-            float v = 0.f;
+        constexpr int kTasks = NR * MF * kWave;
+        for (int e = threadIdx.x; e < kTasks; e += NWK * kWave) {
+            const int l = e % kWave;
+            const int mf = (e / kWave) % MF;
+            const int rr = e / (kWave * MF);
+            const int n0 = ((blockIdx.x * NR + rr) * RF + rf) * 16 + 4 * (l >> 4);
+            const int m = mf * 16 + (l & 15);
+            if (n0 >= N || m >= M) continue;
+            f32x4v v = red[0][rr][mf][l];
 #pragma unroll
-            for (int w = 0; w < NKS; ++w) v += red[w][rr][mf][r][l];
-            const size_t o = (size_t)m * N + n;
+            for (int w = 1; w < NKS; ++w) v += red[w][rr][mf][l];
+            const size_t o = (size_t)m * N + n0;
             if constexpr (EPI == kEpiSilu) {
-                static_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(silu(v));
-            } else if constexpr (EPI == kEpiResidual) {
-                if (split_stride) plane[o] = v;            // partial plane of this K split
-                else static_cast<float*>(out)[o] += v;     // one owner per element
+                // the next projection's activations, row-major or in the
+                // operand layout (N % 32 == 0: n0..n0+3 are 8 contiguous bytes
+                // of one block)
+                uint16_t* dst = static_cast<uint16_t*>(out) +
+                                (kActT ? ((size_t)(m >> 4) * (N >> 5) + (n0 >> 5)) * 512 +
+                                             ((m & 15) + 16 * ((n0 & 31) >> 3)) * 8 + (n0 & 7)
+                                       : o);
+                if (kActT || (vec && n0 + 3 < N)) {
+                    uint2 pk;
+                    pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
+                    pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n0 + r < N) dst[r] = (uint16_t)f32_to_bf16(silu(v[r]));
+                }
+                continue;
+            }
+            float* dst = EPI == kEpiResidual && split_stride ? plane + o : static_cast<float*>(out) + o;
+            if (vec && n0 + 3 < N) {
+                if constexpr (EPI == kEpiResidual)
+                    if (!split_stride) v += *reinterpret_cast<const f32x4v*>(dst);   // one owner per element
+                *reinterpret_cast<f32x4v*>(dst) = v;
             } else {
-                static_cast<float*>(out)[o] = v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (n0 + r >= N) break;
+                    if constexpr (EPI == kEpiResidual)
+                        if (!split_stride) { dst[r] += v[r]; continue; }
+                    dst[r] = v[r];
+                }
             }
         }
     }
@@ -173,7 +214,7 @@ int skinny_cfg(int MF, int N, int epi, int tiled) {
     return (N + 127) / 128 >= 200 ? kCfg8 : kCfg4;
 }
 
-template <int MF, int RF, int NR, int NKS, int U, int EPI>
+template <int MF, int RF, int NR, int NKS, int U, int EPI, bool kActT = false>
 hipError_t launch_shape(const MatmulArgs& a, const uint16_t* act, void* out, int Mc, int ksg,
                         size_t stride, hipStream_t stream) {
     const int rows = 16 * RF * NR;
@@ -183,10 +224,10 @@ hipError_t launch_shape(const MatmulArgs& a, const uint16_t* act, void* out, int
     const uint16_t* W = static_cast<const uint16_t*>(a.W);
     ProfScope prof(a.name, stream, matmul_bytes(a, Mc), 2.0 * Mc * (double)a.N * a.K);
     if (a.tiled) {
-        SV_LAUNCH(prof, (mfma_skinny_kernel<MF, RF, NR, NKS, U, EPI, true>), grid,
+        SV_LAUNCH(prof, (mfma_skinny_kernel<MF, RF, NR, NKS, U, EPI, true, kActT>), grid,
                   NR * NKS * kWave, stream, W, act, Mc, a.N, a.K, sps, out, stride);
-    } else if constexpr (RF == 1) {
-        SV_LAUNCH(prof, (mfma_skinny_kernel<MF, RF, NR, NKS, U, EPI, false>), grid,
+    } else if constexpr (RF == 1 && !kActT) {
+        SV_LAUNCH(prof, (mfma_skinny_kernel<MF, RF, NR, NKS, U, EPI, false, false>), grid,
                   NR * NKS * kWave, stream, W, act, Mc, a.N, a.K, sps, out, stride);
     } else {
         return hipErrorInvalidValue;
@@ -197,24 +238,43 @@ hipError_t launch_shape(const MatmulArgs& a, const uint16_t* act, void* out, int
 template <int MF, int EPI>
 hipError_t launch_mf(const MatmulArgs& a, const uint16_t* act, void* out, int Mc, int ksg,
                      size_t stride, hipStream_t stream) {
-    if constexpr (MF == 1) {
-        // 9..16 rows: every activation load is as large as the weight load
-        // it meets, so wide projections share it between two fragments
-        if (Mc > 8 && a.N >= 8192 && a.tiled)
-            return launch_shape<1, 2, 1, 4, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
-        return launch_shape<1, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
+    if (a.act_tiled) {
+        // activations in the operand layout (17..128 rows per pass): each
+        // activation load is one contiguous KiB.  The LM head keeps eight
+        // fragments per wave up to 64 rows; the projections run four
+        // fragments per wave and eight k slices (two-step buffers up to 64
+        // rows, one above).
+        if (!a.tiled) return hipErrorInvalidValue;
+        if constexpr (EPI == kEpiStore && MF >= 2 && MF <= 4) {
+            if (skinny_cfg(MF, a.N, EPI, 1) == kCfg8R2)
+                return launch_shape<MF, 8, 2, 2, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
+            return launch_shape<MF, 8, 1, 4, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
+        }
+        return launch_shape<MF, 4, 1, 8, (MF <= 4 ? 2 : 1), EPI, true>(a, act, out, Mc, ksg, stride,
+                                                                        stream);
     }
-    switch (skinny_cfg(MF, a.N, EPI, a.tiled)) {
-        case kCfg1: return launch_shape<MF, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
-        case kCfg4:
-            if constexpr (EPI != kEpiResidual)
-                return launch_shape<MF, 4, 1, 4, 2, EPI>(a, act, out, Mc, ksg, stride, stream);
-            return hipErrorInvalidValue;
-        case kCfg8: return launch_shape<MF, 8, 1, 4, 1, EPI>(a, act, out, Mc, ksg, stride, stream);
-        default:
-            if constexpr (EPI == kEpiStore)
-                return launch_shape<MF, 8, 2, 2, 1, EPI>(a, act, out, Mc, ksg, stride, stream);
-            return hipErrorInvalidValue;
+    if constexpr (MF > 4) {
+        return hipErrorInvalidValue;     // row-major activations: passes of at most 64 rows
+    } else {
+        if constexpr (MF == 1) {
+            // 9..16 rows: every activation load is as large as the weight load
+            // it meets, so wide projections share it between two fragments
+            if (Mc > 8 && a.N >= 8192 && a.tiled)
+                return launch_shape<1, 2, 1, 4, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
+            return launch_shape<1, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
+        }
+        switch (skinny_cfg(MF, a.N, EPI, a.tiled)) {
+            case kCfg1: return launch_shape<MF, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
+            case kCfg4:
+                if constexpr (EPI != kEpiResidual)
+                    return launch_shape<MF, 4, 1, 4, 2, EPI>(a, act, out, Mc, ksg, stride, stream);
+                return hipErrorInvalidValue;
+            case kCfg8: return launch_shape<MF, 8, 1, 4, 1, EPI>(a, act, out, Mc, ksg, stride, stream);
+            default:
+                if constexpr (EPI == kEpiStore)
+                    return launch_shape<MF, 8, 2, 2, 1, EPI>(a, act, out, Mc, ksg, stride, stream);
+                return hipErrorInvalidValue;
+        }
     }
 }
 
@@ -225,8 +285,12 @@ hipError_t launch_skinny_epi(const MatmulArgs& a, hipStream_t stream) {
     const bool planes = EPI == kEpiResidual && a.splits > 0;
     const int ksg = planes ? a.splits : 1;
     const size_t stride = planes ? (size_t)a.M * a.N : 0;
-    for (int mb = 0; mb < a.M; mb += 64) {
-        const int Mc = a.M - mb < 64 ? a.M - mb : 64;
+    // passes of 64 rows (row-major activations) or 128 (operand layout); a
+    // pass starts on a 16-row block, so both layouts offset it by mb * K
+    // elements (activations) and mb * N (outputs)
+    const int pass = a.act_tiled ? 128 : 64;
+    for (int mb = 0; mb < a.M; mb += pass) {
+        const int Mc = a.M - mb < pass ? a.M - mb : pass;
         const uint16_t* act = static_cast<const uint16_t*>(a.act) + (size_t)mb * a.K;
         void* out = static_cast<char*>(a.out) + (size_t)mb * a.N * out_es;
         hipError_t e;
@@ -234,7 +298,11 @@ hipError_t launch_skinny_epi(const MatmulArgs& a, hipStream_t stream) {
             case 1: e = launch_mf<1, EPI>(a, act, out, Mc, ksg, stride, stream); break;
             case 2: e = launch_mf<2, EPI>(a, act, out, Mc, ksg, stride, stream); break;
             case 3: e = launch_mf<3, EPI>(a, act, out, Mc, ksg, stride, stream); break;
-            default: e = launch_mf<4, EPI>(a, act, out, Mc, ksg, stride, stream); break;
+            case 4: e = launch_mf<4, EPI>(a, act, out, Mc, ksg, stride, stream); break;
+            case 5: e = launch_mf<5, EPI>(a, act, out, Mc, ksg, stride, stream); break;
+            case 6: e = launch_mf<6, EPI>(a, act, out, Mc, ksg, stride, stream); break;
+            case 7: e = launch_mf<7, EPI>(a, act, out, Mc, ksg, stride, stream); break;
+            default: e = launch_mf<8, EPI>(a, act, out, Mc, ksg, stride, stream); break;
         }
         if (e != hipSuccess) return e;
     }
@@ -243,12 +311,12 @@ hipError_t launch_skinny_epi(const MatmulArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int skinny_splits(int M, int N, int K, int tiled) {
-    // 17+ rows run eight fragments per wave, so a d-row down projection has
-    // few workgroups: split K until the grid fills 256 CUs (>= 16 steps of 32
-    // per split half, so every k slice keeps a few steps)
+int skinny_splits(int M, int N, int K, int tiled, int act_tiled) {
+    // 17+ rows run four or eight fragments per wave, so a d-row down
+    // projection has few workgroups: split K until the grid fills 256 CUs
+    // (>= 16 steps of 32 per split half, so every k slice keeps a few steps)
     if (!tiled || M <= 16) return 0;
-    const long long wg = (N + 127) / 128;
+    const long long wg = (N + (act_tiled ? 63 : 127)) / (act_tiled ? 64 : 128);
     int ksg = 1;
     while (wg * ksg < 256 && ksg < 8 && (K / 32) / (ksg * 2) >= 16) ksg *= 2;
     return ksg > 1 ? ksg : 0;
@@ -256,6 +324,7 @@ int skinny_splits(int M, int N, int K, int tiled) {
 
 hipError_t launch_mfma_skinny(const MatmulArgs& a, hipStream_t stream) {
     if (!a.bf16 || a.K % 32) return hipErrorInvalidValue;
+    if (a.act_tiled && (!a.tiled || (a.epi == kEpiSilu && a.N % 32))) return hipErrorInvalidValue;
     switch (a.epi) {
         case kEpiSilu: return launch_skinny_epi<kEpiSilu>(a, stream);
         case kEpiResidual: return launch_skinny_epi<kEpiResidual>(a, stream);

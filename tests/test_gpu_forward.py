@@ -41,7 +41,7 @@ def test_tiny_fp32_forward():
 
 @gpu
 @pytest.mark.parametrize("tiled", [False, True])
-@pytest.mark.parametrize("M", [1, 3, 5, 8, 9, 16, 40, 64, 130, 320])
+@pytest.mark.parametrize("M", [1, 3, 5, 8, 9, 16, 17, 33, 40, 64, 65, 128, 129, 320])
 def test_small_bf16_forward_rows(M, tiled):
     sv = require_gpu()
     # several tiles in every dimension plus a ragged vocabulary
@@ -70,11 +70,13 @@ def test_wide_projections_two_fragments_per_wave(M):
 
 @gpu
 @pytest.mark.parametrize("kind", ["skinny", "tiled"])
-@pytest.mark.parametrize("M", [17, 40, 64, 100])
+@pytest.mark.parametrize("M", [17, 40, 64, 100, 128, 160])
 def test_bf16_forward_kernel_families(M, kind, monkeypatch):
     """Both MFMA families at rows where either may run (the choice can be
     forced for measurement); a long down projection makes both split K into
-    partial planes that the next norm folds in."""
+    partial planes that the next norm folds in.  From 17 rows the streaming
+    kernel reads operand-layout activations in passes of 128 rows (160: a
+    second pass of 32)."""
     sv = require_gpu()
     monkeypatch.setenv("SPEC_VERIFY_MATMUL", kind)
     w = workload.Workload("split-bf16", 512, 4096, 2, 1001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 2)

@@ -261,6 +261,11 @@ hipError_t launch_mf(const MatmulArgs& a, const uint16_t* act, void* out, int Mc
             // it meets, so wide projections share it between two fragments
             if (Mc > 8 && a.N >= 8192 && a.tiled)
                 return launch_shape<1, 2, 1, 4, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
+            // the up projection's short reduction (d) in 16 slices of
+            // two-step buffers: 3% faster than 8 slices on the 8B shape, where
+            // the down projection (K = ffn) and the head are not
+            if (EPI == kEpiSilu && Mc <= 8 && a.tiled)
+                return launch_shape<1, 1, 1, 16, 2, EPI>(a, act, out, Mc, ksg, stride, stream);
             return launch_shape<1, 1, 1, 8, 4, EPI>(a, act, out, Mc, ksg, stride, stream);
         }
         switch (skinny_cfg(MF, a.N, EPI, a.tiled)) {

@@ -58,18 +58,8 @@ int forced_kind() {
     return k;
 }
 
-// From kTiledMinRows rows the weights are reused from LDS (kMfmaTiled); below
-// it every weight is streamed once per pass of up to 128 rows (kMfmaSkinny).
-// From kActTiledMinRows rows the streaming kernel reads its activations in
-// the operand layout (one contiguous KiB per 16 rows x 32 k) instead of
-// row-major (16 rows x 64 bytes at a row stride): measured on the 8B-shaped
-// stack, 0.478 vs 0.520 ms per forward at 17 rows and 0.553 vs 0.660 at 64.
-// Below it row-major wins, since rows past M cost nothing there.
-constexpr int kTiledMinRows = 129;
-constexpr int kActTiledMinRows = 17;
-// The LM head moves to the LDS-staged GEMM earlier: 65+ rows (measured on the
-// 8B-shaped head at 96 and 128 rows: 64 and 66 us vs 79 and 79 us streamed).
-constexpr int kHeadTiledMinRows = 65;
+// Kernel family per row count: kTiledMinRows, kHeadTiledMinRows and
+// kActTiledMinRows (kernels.hpp).
 
 int matmul_kind(const sv_model_desc& d, int M, bool head = false) {
     if (d.wdtype != SV_BF16) return kGemvValu;

@@ -75,6 +75,20 @@ struct MoeFold {
 hipError_t launch_rmsnorm_moe(float* h, const MoeFold& fold, const float* gain, void* act, int M,
                               int d, float eps, int act_tiled, hipStream_t stream);
 
+// Kernel family and activation layout by row count (bf16, tiled weights),
+// measured on the 8B-shaped stack:
+//  - the projections stream their weights up to kTiledMinRows - 1 rows per
+//    pass and reuse them from LDS from kTiledMinRows on (LDS-staged GEMM);
+//    the LM head moves to the GEMM from kHeadTiledMinRows (57-61 vs 79 us
+//    streamed at 96-128 rows);
+//  - from kActTiledMinRows rows the activations are in the operand layout
+//    (one contiguous KiB per 16 rows x 32 k) for both families; below it they
+//    are row-major, where rows past M cost nothing (forward at 9 / 16 rows:
+//    0.429 / 0.434 vs 0.454 / 0.491 ms row-major; at 5 rows 0.421 vs 0.398).
+constexpr int kTiledMinRows = 129;
+constexpr int kHeadTiledMinRows = 65;
+constexpr int kActTiledMinRows = 9;
+
 // Split count of the LDS-staged GEMM's K range for an [M, N, K] product
 // (so that the tile grid fills the chip).
 int tiled_splits(int M, int N, int K);

@@ -433,6 +433,7 @@ size_t aup(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MoePlan {
     int head_kind = kMfmaSkinny;
+    int head_act_tiled = 0;    // the last norm writes the head's activations in the operand layout
     int router_spw = 0, router_splits = 0;   // reduction steps per router split, splits
     size_t off_h, off_a, off_part, off_sel, off_w, off_offs, off_list, off_perm, off_inv, off_s,
         off_y, bytes;
@@ -441,7 +442,8 @@ struct MoePlan {
 MoePlan plan_moe(const sv_moe_desc& d, int M) {
     MoePlan p{};
     const size_t Mk = (size_t)M * d.top_k;
-    p.head_kind = M >= 65 ? kMfmaTiled : kMfmaSkinny;
+    p.head_kind = M >= kHeadTiledMinRows ? kMfmaTiled : kMfmaSkinny;
+    p.head_act_tiled = M >= kActTiledMinRows;
     const int S = d.d / 32;
     p.router_spw = S / 16 > 8 ? (S + 15) / 16 : 8;    // at most 16 partial score planes
     p.router_splits = (S + p.router_spw - 1) / p.router_spw;
@@ -560,7 +562,7 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
     hipError_t e;
 
     e = launch_rmsnorm(hidden, h, nullptr, 0, d.gain, a, M, d.d, d.rms_eps, 1,
-                       d.n_layers == 0 && p.head_kind == kMfmaTiled, s);
+                       d.n_layers == 0 && p.head_act_tiled, s);
     if (e != hipSuccess) return moe_hip_fail(e, "rmsnorm launch");
     for (int l = 0; l < d.n_layers; ++l) {
         const uint16_t* wr = static_cast<const uint16_t*>(d.w_router) + (size_t)l * router_stride;
@@ -617,7 +619,7 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
         fold.inv = inv;
         fold.k = k;
         e = launch_rmsnorm_moe(h, fold, d.gain + (size_t)(l + 1) * d.d, a, M, d.d, d.rms_eps,
-                               l + 1 == d.n_layers && p.head_kind == kMfmaTiled, s);
+                               l + 1 == d.n_layers && p.head_act_tiled, s);
         if (e != hipSuccess) return moe_hip_fail(e, "rmsnorm launch");
     }
     MatmulArgs hd{};
@@ -625,7 +627,7 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
     hd.act = a;
     hd.M = M; hd.N = d.vocab; hd.K = d.d;
     hd.epi = kEpiStore; hd.out = logits; hd.bf16 = 1; hd.tiled = 1;
-    hd.act_tiled = p.head_kind == kMfmaTiled;
+    hd.act_tiled = p.head_act_tiled;
     e = launch_matmul(hd, p.head_kind, s);
     if (e != hipSuccess) return moe_hip_fail(e, "LM-head launch");
     return SV_OK;

@@ -41,7 +41,7 @@ def test_tiny_fp32_forward():
 
 @gpu
 @pytest.mark.parametrize("tiled", [False, True])
-@pytest.mark.parametrize("M", [1, 3, 5, 8, 9, 16, 17, 33, 40, 64, 65, 128, 129, 320])
+@pytest.mark.parametrize("M", [1, 3, 5, 8, 9, 12, 16, 17, 33, 40, 64, 65, 128, 129, 320])
 def test_small_bf16_forward_rows(M, tiled):
     sv = require_gpu()
     # several tiles in every dimension plus a ragged vocabulary
@@ -55,10 +55,10 @@ def test_small_bf16_forward_rows(M, tiled):
 
 @gpu
 @pytest.mark.parametrize("M", [9, 12, 16])
-def test_wide_projections_two_fragments_per_wave(M):
-    """9..16 rows on projections of 8192+ outputs run two weight fragments
-    per wave (up: ffn 8256; head: V 9001 = 563 fragments, so the last
-    workgroup's second fragment is clamped and its outputs skipped)."""
+def test_wide_projections_ragged_fragments(M):
+    """9..16 rows (operand-layout activations, four weight fragments per
+    wave) on projections of 8192+ outputs: up ffn 8256; head V 9001 = 563
+    fragments, so the last workgroup holds three and skips the fourth."""
     sv = require_gpu()
     w = workload.Workload("wide-bf16", 256, 8256, 2, 9001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 3)
     model = workload.make_model(w, draft_head=False)

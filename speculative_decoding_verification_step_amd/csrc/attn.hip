@@ -45,9 +45,19 @@ constexpr float kLazyMargin = 8.0f;   // log2 units a score may exceed the runni
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// Query tiles (16 rows each) per wave: every K/V block a wave loads serves QT
+// tiles.  Two at head_dim 128 and four at 64 keep a wave's registers within
+// its share (two K/V register sets of 64 / 32 VGPRs plus QT accumulators).
+int tiles_per_wave(int nq, int Dh) {
+    if (nq <= 1) return 1;
+    if (nq == 2) return 2;
+    return Dh == 128 ? 2 : 4;
+}
+
 struct AttnPlan {
-    int G = 0, nq = 0, nsplit = 1, bps = 0;
-    long long units = 0;
+    int G = 0, nq = 0, qt = 1, nqg = 0, nsplit = 1, bps = 0;
+    long long units = 0;     // workgroups: (request, KV head, split, group of qt tiles)
+    long long rows16 = 0;    // 16-row partial-state slots: (request, KV head, split, tile)
     size_t ws_bytes = 0;
 };
 
@@ -55,7 +65,9 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int Dh, int max_blocks) {
     AttnPlan p;
     p.G = Hq / Hkv;
     p.nq = (p.G * T + 15) / 16;
-    const long long base = (long long)B * Hkv * p.nq;
+    p.qt = tiles_per_wave(p.nq, Dh);
+    p.nqg = (p.nq + p.qt - 1) / p.qt;
+    const long long base = (long long)B * Hkv * p.nqg;
     long long ns = (kTargetUnits + base - 1) / base;
     ns = ns < 1 ? 1 : ns;
     const long long cap = max_blocks / kMinBlocksPerSplit > 0 ? max_blocks / kMinBlocksPerSplit : 1;
@@ -63,8 +75,9 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int Dh, int max_blocks) {
     p.bps = (int)((max_blocks + ns - 1) / ns);
     p.nsplit = (max_blocks + p.bps - 1) / p.bps;
     p.units = base * p.nsplit;
-    // partial output rows (16 per unit) and their (max, sum) pairs
-    p.ws_bytes = p.nsplit > 1 ? (size_t)p.units * 16 * (Dh + 2) * 4 : 0;
+    p.rows16 = (long long)B * Hkv * p.nq * p.nsplit;
+    // partial output rows (16 per tile and split) and their (max, sum) pairs
+    p.ws_bytes = p.nsplit > 1 ? (size_t)p.rows16 * 16 * (Dh + 2) * 4 : 0;
     return p;
 }
 
@@ -74,10 +87,10 @@ struct AttnArgs {
     const uint16_t* vc;
     const int32_t* table;
     const int32_t* ctx;
-    int B, T, Hq, Hkv, max_blocks, num_blocks, nq, nsplit, bps;
+    int B, T, Hq, Hkv, max_blocks, num_blocks, nq, nqg, nsplit, bps;
     float scale_log2;     // softmax scale times log2(e): scores in the exp2 domain
-    float* part_o;        // [units*16, Dh] unnormalised partial outputs (split runs)
-    float* part_ml;       // [units*16, 2] partial (max, sum)
+    float* part_o;        // [rows16*16, Dh] unnormalised partial outputs (split runs)
+    float* part_ml;       // [rows16*16, 2] partial (max, sum)
     float* out;           // [B, T, Hq, Dh]
 };
 
@@ -88,49 +101,65 @@ struct KVRegs {
     bf16x8 k0[DH / 32], k1[DH / 32], v[DH / 16];
 };
 
-template <int DH, bool kDirect>
-__global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void attn_kernel(AttnArgs a) {
+template <int DH, bool kDirect, int QT>
+__global__ __launch_bounds__(kWavesPerGroup * kWave, QT == 1 ? 2 : 1) void attn_kernel(AttnArgs a) {
     constexpr int KS = DH / 32;   // k steps of the score product
     constexpr int DT = DH / 16;   // 16-dim tiles of the output
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     // XCD-contiguous renumbering (workgroup i runs on XCD i % 8): the query
-    // tiles of one (request, KV head, range) get consecutive numbers on one
-    // XCD and read its blocks through one L2
+    // tile groups of one (request, KV head, range) get consecutive numbers on
+    // one XCD and read its blocks through one L2
     const int wg = blockIdx.x, Gn = gridDim.x;
     const int q8 = Gn / 8, r8 = Gn % 8, x8 = wg % 8, j8 = wg / 8;
     const long long unit = x8 < r8 ? x8 * (q8 + 1) + j8 : r8 * (q8 + 1) + (x8 - r8) * q8 + j8;
-    const int qt = (int)(unit % a.nq);
-    long long rest = unit / a.nq;
+    const int qg = (int)(unit % a.nqg);
+    long long rest = unit / a.nqg;
     const int sp = (int)(rest % a.nsplit);
     rest /= a.nsplit;
     const int kvh = (int)(rest % a.Hkv);
     const int b = (int)(rest / a.Hkv);
     const int G = a.Hq / a.Hkv;
     const int c = lane & 15, g = lane >> 4;
-
-    // this lane's query row: position t, head h (column of S^T)
-    const int r = qt * 16 + c;
-    const bool row_ok = r < G * a.T;
-    const int t = row_ok ? r / G : 0;
-    const int h = kvh * G + r % G;
     const int cap = a.max_blocks * kBlk;
     const int ctx = clamp_ctx(a.ctx[b], cap);
-    const int vis = row_ok ? min(ctx + t + 1, cap) : 0;      // visible positions of the row
     const int n_all = min(ctx + a.T, cap);                    // positions any row may see
     const int kb_end = min((n_all + kBlk - 1) / kBlk, (sp + 1) * a.bps);
 
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    bf16x8 qv[KS];
-    const uint16_t* qrow = a.q + (((size_t)b * a.T + t) * a.Hq + (h < a.Hq ? h : 0)) * DH;
+    // this lane's query row in each of the group's tiles: position t, head h
+    // (a column of S^T); tiles past the last one hold no rows
+    int t[QT], h[QT], vis[QT];
+    bool row_ok[QT], tile_ok[QT];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-        qv[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : zero8;
+    for (int i = 0; i < QT; ++i) {
+        const int qt = qg * QT + i;
+        const int r = qt * 16 + c;
+        tile_ok[i] = qt < a.nq;
+        row_ok[i] = r < G * a.T;
+        t[i] = row_ok[i] ? r / G : 0;
+        h[i] = kvh * G + r % G;
+        vis[i] = row_ok[i] ? min(ctx + t[i] + 1, cap) : 0;    // visible positions of the row
+    }
 
-    float m = -INFINITY, lpart = 0.f;
-    f32x4v acc[DT];
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    bf16x8 qv[QT][KS];
 #pragma unroll
-    for (int u = 0; u < DT; ++u) acc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < QT; ++i) {
+        const uint16_t* qrow = a.q + (((size_t)b * a.T + t[i]) * a.Hq + (h[i] < a.Hq ? h[i] : 0)) * DH;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qv[i][s] = row_ok[i] ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : zero8;
+    }
+
+    float m[QT], lpart[QT];
+    f32x4v acc[QT][DT];
+#pragma unroll
+    for (int i = 0; i < QT; ++i) {
+        m[i] = -INFINITY;
+        lpart[i] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) acc[i][u] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int32_t* trow = a.table + (size_t)b * a.max_blocks;
     auto load = [&](KVRegs<DH>& kv, int kb) {
@@ -152,51 +181,55 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void attn_kernel(AttnArg
         }
     };
     auto process = [&](const KVRegs<DH>& kv, int kb) {
-        f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k0[s], qv[s], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k1[s], qv[s], s1, 0, 0, 0);
+        for (int i = 0; i < QT; ++i) {
+            if (!tile_ok[i]) continue;                       // uniform over the workgroup
+            f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k0[s], qv[i][s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k1[s], qv[i][s], s1, 0, 0, 0);
+            }
+            // lane holds S^T[key 4g+j][row] in s0[j] and S^T[key 16+4g+j][row] in s1[j]
+            const int p0 = kb * kBlk + 4 * g;
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[j] = p0 + j < vis[i] ? s0[j] * a.scale_log2 : -INFINITY;
+                x[4 + j] = p0 + 16 + j < vis[i] ? s1[j] * a.scale_log2 : -INFINITY;
+            }
+            // Lazy running max: the reference m (equal in the row's four lane
+            // groups) moves only when some score exceeds it by more than
+            // kLazyMargin (log2 units), found with one wave-wide vote; the
+            // exact row max and the rescale then run.  Otherwise p <= 2^margin
+            // and no cross-lane exchange is needed; the sum stays per lane group.
+            float lm = x[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) lm = fmaxf(lm, x[j]);
+            if (__ballot(lm > m[i] + kLazyMargin)) {
+                float bm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
+                bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+                const float mn = fmaxf(m[i], bm);
+                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
+                lpart[i] *= alpha;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) acc[i][u] *= alpha;
+                m[i] = mn;
+            }
+            const float mref = m[i] == -INFINITY ? 0.f : m[i];   // no visible key yet: p = 0
+            uint32_t pb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pb[j] = f32_to_bf16(__builtin_amdgcn_exp2f(x[j] - mref));
+                lpart[i] += __uint_as_float(pb[j] << 16);
+            }
+            const bf16x8 pv = __builtin_bit_cast(
+                bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                              pb[6] | (pb[7] << 16)});
+#pragma unroll
+            for (int u = 0; u < DT; ++u)
+                acc[i][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.v[u], pv, acc[i][u], 0, 0, 0);
         }
-        // lane holds S^T[key 4g+i][row] in s0[i] and S^T[key 16+4g+i][row] in s1[i]
-        const int p0 = kb * kBlk + 4 * g;
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = p0 + i < vis ? s0[i] * a.scale_log2 : -INFINITY;
-            x[4 + i] = p0 + 16 + i < vis ? s1[i] * a.scale_log2 : -INFINITY;
-        }
-        // Lazy running max: the reference m (equal in the row's four lane
-        // groups) moves only when some score exceeds it by more than
-        // kLazyMargin (log2 units), found with one wave-wide vote; the
-        // exact row max and the rescale then run.  Otherwise p <= 2^margin
-        // and no cross-lane exchange is needed; the sum stays per lane group.
-        float lm = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
-        if (__ballot(lm > m + kLazyMargin)) {
-            float bm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
-            bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-            const float mn = fmaxf(m, bm);
-            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-            lpart *= alpha;
-#pragma unroll
-            for (int u = 0; u < DT; ++u) acc[u] *= alpha;
-            m = mn;
-        }
-        const float mref = m == -INFINITY ? 0.f : m;          // no visible key yet: p = 0
-        uint32_t pb[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            pb[i] = f32_to_bf16(__builtin_amdgcn_exp2f(x[i] - mref));
-            lpart += __uint_as_float(pb[i] << 16);
-        }
-        const bf16x8 pv = __builtin_bit_cast(
-            bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                          pb[6] | (pb[7] << 16)});
-#pragma unroll
-        for (int u = 0; u < DT; ++u)
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.v[u], pv, acc[u], 0, 0, 0);
     };
 
     // this wave's blocks: kb0 + wave, + 4, + 8, ..., the next one always in
@@ -222,51 +255,57 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void attn_kernel(AttnArg
         }
     }
 
-    // the row's softmax sum over its four lane groups
-    float l = lpart + __shfl_xor(lpart, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-
-    // merge the four waves' states (fixed wave order); lane holds O^T[dim
-    // 16u+4g+i][row] in acc[u][i], and (m, l) of its row
+    // merge the four waves' states (fixed wave order), one tile at a time;
+    // lane holds O^T[dim 16u+4g+j][row] in acc[i][u][j], and (m, l) of its row
     __shared__ float sm[kWavesPerGroup][16], sl[kWavesPerGroup][16];
     __shared__ f32x4v so[kWavesPerGroup][DT][kWave];
-    if (g == 0) {
-        sm[wave][c] = m;
-        sl[wave][c] = l;
-    }
 #pragma unroll
-    for (int u = 0; u < DT; ++u) so[wave][u][lane] = acc[u];
-    __syncthreads();
-    float M = sm[0][c];
-#pragma unroll
-    for (int w = 1; w < kWavesPerGroup; ++w) M = fmaxf(M, sm[w][c]);
-    float e[kWavesPerGroup], L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w) {
-        e[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][c] - M);
-        L += e[w] * sl[w][c];
-    }
-    // wave w finishes the output tiles u = w, w + 4, ...
-    const size_t prow = (size_t)unit * 16 + c;
-#pragma unroll
-    for (int u = wave; u < DT; u += kWavesPerGroup) {
-        f32x4v o = e[0] * so[0][u][lane];
-#pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) o += e[w] * so[w][u][lane];
-        if constexpr (kDirect) {
-            if (row_ok) {
-                const float inv = L > 0.f ? 1.0f / L : 0.f;
-                *reinterpret_cast<f32x4v*>(a.out + (((size_t)b * a.T + t) * a.Hq + h) * DH +
-                                           16 * u + 4 * g) = o * inv;
-            }
-        } else {
-            *reinterpret_cast<f32x4v*>(a.part_o + prow * DH + 16 * u + 4 * g) = o;
+    for (int i = 0; i < QT; ++i) {
+        if (!tile_ok[i]) continue;                           // uniform over the workgroup
+        // the row's softmax sum over its four lane groups
+        float l = lpart[i] + __shfl_xor(lpart[i], 16, kWave);
+        l += __shfl_xor(l, 32, kWave);
+        if (i) __syncthreads();                              // the previous tile's readers are done
+        if (g == 0) {
+            sm[wave][c] = m[i];
+            sl[wave][c] = l;
         }
-    }
-    if constexpr (!kDirect) {
-        if (wave == 0 && g == 0) {
-            a.part_ml[2 * prow] = M;
-            a.part_ml[2 * prow + 1] = L;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) so[wave][u][lane] = acc[i][u];
+        __syncthreads();
+        float M = sm[0][c];
+#pragma unroll
+        for (int w = 1; w < kWavesPerGroup; ++w) M = fmaxf(M, sm[w][c]);
+        float e[kWavesPerGroup], L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) {
+            e[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][c] - M);
+            L += e[w] * sl[w][c];
+        }
+        // the partial-state slot of this tile: (request, KV head, split, tile)
+        const long long slot = (((long long)b * a.Hkv + kvh) * a.nsplit + sp) * a.nq + qg * QT + i;
+        const size_t prow = (size_t)slot * 16 + c;
+        // wave w finishes the output tiles u = w, w + 4, ...
+#pragma unroll
+        for (int u = wave; u < DT; u += kWavesPerGroup) {
+            f32x4v o = e[0] * so[0][u][lane];
+#pragma unroll
+            for (int w = 1; w < kWavesPerGroup; ++w) o += e[w] * so[w][u][lane];
+            if constexpr (kDirect) {
+                if (row_ok[i]) {
+                    const float inv = L > 0.f ? 1.0f / L : 0.f;
+                    *reinterpret_cast<f32x4v*>(a.out + (((size_t)b * a.T + t[i]) * a.Hq + h[i]) * DH +
+                                               16 * u + 4 * g) = o * inv;
+                }
+            } else {
+                *reinterpret_cast<f32x4v*>(a.part_o + prow * DH + 16 * u + 4 * g) = o;
+            }
+        }
+        if constexpr (!kDirect) {
+            if (wave == 0 && g == 0) {
+                a.part_ml[2 * prow] = M;
+                a.part_ml[2 * prow + 1] = L;
+            }
         }
     }
 }
@@ -416,12 +455,12 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
     a.ctx = ctx_len;
     a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv;
     a.max_blocks = max_blocks; a.num_blocks = num_blocks;
-    a.nq = p.nq; a.nsplit = p.nsplit; a.bps = p.bps;
+    a.nq = p.nq; a.nqg = p.nqg; a.nsplit = p.nsplit; a.bps = p.bps;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
     if (p.nsplit > 1) {
         a.part_o = static_cast<float*>(ws);
-        a.part_ml = a.part_o + (size_t)p.units * 16 * head_dim;
+        a.part_ml = a.part_o + (size_t)p.rows16 * 16 * head_dim;
     }
     const unsigned grid = (unsigned)p.units;
     // algorithmic bytes: every visible key and value once per (request, KV head) at the
@@ -430,22 +469,31 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
     const double flops = 4.0 * B * Hq * T * (double)max_blocks * kBlk * head_dim;
     {
         ProfScope prof("attention", stream, kv_bytes + (double)B * T * Hq * head_dim * 6, flops);
-#define SV_ATTN(DH, DIRECT)                                                                 \
-        SV_LAUNCH(prof, (attn_kernel<DH, DIRECT>), grid, kWavesPerGroup * kWave, stream, a)
+#define SV_ATTN(DH, DIRECT, QT)                                                             \
+        SV_LAUNCH(prof, (attn_kernel<DH, DIRECT, QT>), grid, kWavesPerGroup * kWave, stream, a)
+        // tiles per wave: 1 or 2 at head_dim 128, 1, 2 or 4 at 64 (tiles_per_wave)
+#define SV_ATTN_128(DIRECT)                                                                 \
+        if (p.qt == 1) SV_ATTN(128, DIRECT, 1); else SV_ATTN(128, DIRECT, 2);
+#define SV_ATTN_64(DIRECT)                                                                  \
+        if (p.qt == 1) SV_ATTN(64, DIRECT, 1);                                              \
+        else if (p.qt == 2) SV_ATTN(64, DIRECT, 2);                                         \
+        else SV_ATTN(64, DIRECT, 4);
         if (head_dim == 128) {
-            if (p.nsplit > 1) SV_ATTN(128, false); else SV_ATTN(128, true);
+            if (p.nsplit > 1) { SV_ATTN_128(false) } else { SV_ATTN_128(true) }
         } else {
-            if (p.nsplit > 1) SV_ATTN(64, false); else SV_ATTN(64, true);
+            if (p.nsplit > 1) { SV_ATTN_64(false) } else { SV_ATTN_64(true) }
         }
+#undef SV_ATTN_64
+#undef SV_ATTN_128
 #undef SV_ATTN
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return launch_fail(e, "attention launch");
     if (p.nsplit > 1) {
-        const long long threads = (long long)B * Hkv * p.nq * 16 * (head_dim / 4);
+        const long long threads = (long long)B * Hkv * p.nq * 16 * (head_dim / 4);   // (request, KV head, tile, row, dim/4)
         const unsigned cgrid = (unsigned)((threads + 255) / 256);
         ProfScope prof("attention_combine", stream,
-                       (double)p.units * 16 * (head_dim + 2) * 4 + (double)B * T * Hq * head_dim * 4,
+                       (double)p.rows16 * 16 * (head_dim + 2) * 4 + (double)B * T * Hq * head_dim * 4,
                        0.0);
         if (head_dim == 128)
             SV_LAUNCH(prof, attn_combine_kernel<128>, cgrid, 256, stream, a);

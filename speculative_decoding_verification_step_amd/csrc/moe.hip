@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
     const int s0 = S * wave / kGroupWaves, s1 = S * (wave + 1) / kGroupWaves;
     const uint16_t* wbase = W + (size_t)e * wstride + lane * 8;
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    __shared__ float red[kGroupWaves][RF][MF][4][kWave];
+    __shared__ f32x4v red[kGroupWaves][RF][MF][kWave];
 
     bf16x8 wa[U][RF], wb[U][RF], xa[U][MF], xb[U][MF];
     auto loadw = [&](bf16x8 (&w)[U][RF], int s) {
@@ -401,28 +401,48 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
             loadx(xa, s + 2 * U);
             compute(wb, xb);
         }
+        // the k slices summed in wave order: each wave stores its accumulators
+        // lane-major (16-byte LDS writes), and each task sums the copies of one
+        // lane's four outputs n0..n0+3 of one row (16-byte reads, no bank
+        // conflicts) and stores them together
         if (pass) __syncthreads();         // the previous pass's readers are done
 #pragma unroll
         for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
-            for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) red[wave][rf][mf][r][lane] = acc[rf][mf][r];
+            for (int mf = 0; mf < MF; ++mf) red[wave][rf][mf][lane] = acc[rf][mf];
         __syncthreads();
-        for (int i = threadIdx.x; i < 256 * MF * RF; i += kGroupWaves * kWave) {
-            const int ii = i & 15, jj = (i >> 4) & 15, mf = (i >> 8) % MF, rf = (i >> 8) / MF;
-            const int n = (f0 + rf) * 16 + ii;
-            const int j = pass + mf * 16 + jj;
-            if (n >= N || j >= rows) continue;
-            const int r = ii & 3, l = ((ii >> 2) << 4) + jj;
-            float v = 0.f;
+        for (int i = threadIdx.x; i < kWave * MF * RF; i += kGroupWaves * kWave) {
+            const int l = i % kWave, mf = (i / kWave) % MF, rf = i / (kWave * MF);
+            const int n0 = (f0 + rf) * 16 + 4 * (l >> 4);
+            const int j = pass + mf * 16 + (l & 15);
+            if (n0 >= N || j >= rows) continue;
+            f32x4v v = red[0][rf][mf][l];
 #pragma unroll
-            for (int w = 0; w < kGroupWaves; ++w) v += red[w][rf][mf][r][l];
-            const size_t o = (size_t)(row0 + j) * N + n;
-            if constexpr (EPI == kEpiSilu)
-                static_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(silu(v));
-            else
-                static_cast<float*>(out)[o] = v;
+            for (int w = 1; w < kGroupWaves; ++w) v += red[w][rf][mf][l];
+            const size_t o = (size_t)(row0 + j) * N + n0;
+            const bool full = (N & 3) == 0 && n0 + 3 < N;   // rows start 16-byte aligned
+            if constexpr (EPI == kEpiSilu) {
+                uint16_t* dst = static_cast<uint16_t*>(out) + o;
+                if (full) {
+                    uint2 pk;
+                    pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
+                    pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n0 + r < N) dst[r] = (uint16_t)f32_to_bf16(silu(v[r]));
+                }
+            } else {
+                float* dst = static_cast<float*>(out) + o;
+                if (full) {
+                    *reinterpret_cast<f32x4v*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n0 + r < N) dst[r] = v[r];
+                }
+            }
         }
     }
 }

@@ -54,8 +54,19 @@ int tiles_per_wave(int nq, int Dh) {
     return Dh == 128 ? 2 : 4;
 }
 
+// From 4 query tiles per KV head the LDS-ring kernel runs instead: four waves
+// of QTW tiles share one pass of every block (QTW 1 or 2 at head_dim 128, up
+// to 4 at 64).
+int ring_tiles_per_wave(int nq, int Dh) {
+    const int want = (nq + kWavesPerGroup - 1) / kWavesPerGroup;
+    if (want <= 1) return 1;
+    if (want <= 2 || Dh == 128) return 2;
+    return 4;
+}
+
 struct AttnPlan {
     int G = 0, nq = 0, qt = 1, nqg = 0, nsplit = 1, bps = 0;
+    int ring = 0;            // the LDS-ring kernel (qt tiles per wave, 4 waves per group)
     long long units = 0;     // workgroups: (request, KV head, split, group of qt tiles)
     long long rows16 = 0;    // 16-row partial-state slots: (request, KV head, split, tile)
     size_t ws_bytes = 0;
@@ -65,8 +76,10 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int Dh, int max_blocks) {
     AttnPlan p;
     p.G = Hq / Hkv;
     p.nq = (p.G * T + 15) / 16;
-    p.qt = tiles_per_wave(p.nq, Dh);
-    p.nqg = (p.nq + p.qt - 1) / p.qt;
+    p.ring = p.nq >= kWavesPerGroup;
+    p.qt = p.ring ? ring_tiles_per_wave(p.nq, Dh) : tiles_per_wave(p.nq, Dh);
+    const int group = p.ring ? kWavesPerGroup * p.qt : p.qt;    // tiles per workgroup
+    p.nqg = (p.nq + group - 1) / group;
     const long long base = (long long)B * Hkv * p.nqg;
     long long ns = (kTargetUnits + base - 1) / base;
     ns = ns < 1 ? 1 : ns;
@@ -310,6 +323,214 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QT == 1 ? 2 : 1) void attn_
     }
 }
 
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// From 4 query tiles per KV head: the four waves own QTW tiles each (4 * QTW
+// tiles = up to 128 query rows per workgroup) and walk the SAME blocks of the
+// context range, which pass once through a ring of kRingStages LDS stages
+// (global_load_lds_dwordx4, kRingStages - 1 blocks in flight, paced by vmcnt
+// and a bare barrier).  A stage holds the block in operand order: the K
+// tiles as 1 KiB MFMA fragments (lane l: key 16 kt + l % 16, dims 32 s + 8 (l
+// / 16)), then the V^T tiles as 64 16-byte chunks (row c of the tile, keys 8 k
+// .. 8 k + 7) with the chunk index XORed by (c / 4) % 4, so each lane's two
+// 8-byte halves are read without bank conflicts.  Each wave then finishes its
+// own rows over the whole range: no merge between waves.
+constexpr int kRingStages = 4;
+
+template <int DH, bool kDirect, int QTW>
+__global__ __launch_bounds__(kWavesPerGroup * kWave, QTW <= 2 ? 2 : 1) void attn_ring_kernel(AttnArgs a) {
+    constexpr int KS = DH / 32;
+    constexpr int DT = DH / 16;
+    constexpr int NF = 2 * KS + DT;                    // 1 KiB fragments per block
+    static_assert(NF % kWavesPerGroup == 0, "every wave issues the same number of copies");
+    constexpr int PER_WAVE = NF / kWavesPerGroup;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingStages][NF * 512];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int wg = blockIdx.x, Gn = gridDim.x;
+    const int q8 = Gn / 8, r8 = Gn % 8, x8 = wg % 8, j8 = wg / 8;
+    const long long unit = x8 < r8 ? x8 * (q8 + 1) + j8 : r8 * (q8 + 1) + (x8 - r8) * q8 + j8;
+    const int qg = (int)(unit % a.nqg);
+    long long rest = unit / a.nqg;
+    const int sp = (int)(rest % a.nsplit);
+    rest /= a.nsplit;
+    const int kvh = (int)(rest % a.Hkv);
+    const int b = (int)(rest / a.Hkv);
+    const int G = a.Hq / a.Hkv;
+    const int c = lane & 15, g = lane >> 4;
+    const int cap = a.max_blocks * kBlk;
+    const int ctx = clamp_ctx(a.ctx[b], cap);
+    const int n_all = min(ctx + a.T, cap);
+    const int kb0 = sp * a.bps;
+    const int kb_end = min((n_all + kBlk - 1) / kBlk, (sp + 1) * a.bps);
+    const int nblk = kb_end > kb0 ? kb_end - kb0 : 0;
+
+    int t[QTW], h[QTW], vis[QTW];
+    bool row_ok[QTW], tile_ok[QTW];
+#pragma unroll
+    for (int i = 0; i < QTW; ++i) {
+        const int qt = (qg * kWavesPerGroup + wave) * QTW + i;
+        const int r = qt * 16 + c;
+        tile_ok[i] = qt < a.nq;
+        row_ok[i] = r < G * a.T;
+        t[i] = row_ok[i] ? r / G : 0;
+        h[i] = kvh * G + r % G;
+        vis[i] = row_ok[i] ? min(ctx + t[i] + 1, cap) : 0;
+    }
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    bf16x8 qv[QTW][KS];
+#pragma unroll
+    for (int i = 0; i < QTW; ++i) {
+        const uint16_t* qrow = a.q + (((size_t)b * a.T + t[i]) * a.Hq + (h[i] < a.Hq ? h[i] : 0)) * DH;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qv[i][s] = row_ok[i] ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : zero8;
+    }
+    float m[QTW], lpart[QTW];
+    f32x4v acc[QTW][DT];
+#pragma unroll
+    for (int i = 0; i < QTW; ++i) {
+        m[i] = -INFINITY;
+        lpart[i] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) acc[i][u] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // copies of block kb into stage st: fragment f = wave + 4 j of the block
+    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+    const int vrow_c = lane >> 2;                              // V chunk copy: tile row
+    const int vchunk = (lane & 3) ^ ((vrow_c >> 2) & 3);       // ... and its swizzled chunk
+    auto issue = [&](int kb, int st) {
+        int blk = trow[kb];
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        const uint16_t* kbase = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlk * DH;
+        const uint16_t* vbase = a.vc + ((size_t)blk * a.Hkv + kvh) * DH * kBlk;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int f = wave + kWavesPerGroup * j;
+            const uint16_t* src;
+            if (f < 2 * KS) {
+                const int kt = f / KS, s = f % KS;
+                src = kbase + (16 * kt + c) * DH + 32 * s + 8 * g;
+            } else {
+                const int u = f - 2 * KS;
+                src = vbase + (16 * u + vrow_c) * kBlk + 8 * vchunk;
+            }
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&ring[st][f * 512], 16, 0, 0);
+        }
+    };
+
+#pragma unroll
+    for (int p = 0; p < kRingStages - 1; ++p)
+        if (p < nblk) issue(kb0 + p, p);
+    const int sw = (c >> 2) & 3;
+    for (int i = 0; i < nblk; ++i) {
+        // this wave's copies of block i are done once at most kRingStages - 2
+        // later blocks remain in flight; the barrier then also means every
+        // wave has finished reading the stage the next copy overwrites
+        if (i + kRingStages - 2 < nblk) wait_vmcnt<PER_WAVE * (kRingStages - 2)>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (i + kRingStages - 1 < nblk) issue(kb0 + i + kRingStages - 1, (i + kRingStages - 1) % kRingStages);
+        const uint16_t* stage = ring[i % kRingStages];
+        bf16x8 k0[KS], k1[KS], v[DT];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            k0[s] = *reinterpret_cast<const bf16x8*>(stage + s * 512 + lane * 8);
+            k1[s] = *reinterpret_cast<const bf16x8*>(stage + (KS + s) * 512 + lane * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+            const uint16_t* vf = stage + (2 * KS + u) * 512;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vf + (c * 4 + ((g >> 1) ^ sw)) * 8 + 4 * (g & 1));
+            const uint2 hi = *reinterpret_cast<const uint2*>(vf + (c * 4 + ((2 + (g >> 1)) ^ sw)) * 8 + 4 * (g & 1));
+            v[u] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
+        const int kb = kb0 + i;
+#pragma unroll
+        for (int q = 0; q < QTW; ++q) {
+            if (!tile_ok[q]) continue;                         // uniform over the wave
+            f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[s], qv[q][s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qv[q][s], s1, 0, 0, 0);
+            }
+            const int p0 = kb * kBlk + 4 * g;
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[j] = p0 + j < vis[q] ? s0[j] * a.scale_log2 : -INFINITY;
+                x[4 + j] = p0 + 16 + j < vis[q] ? s1[j] * a.scale_log2 : -INFINITY;
+            }
+            float lm = x[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) lm = fmaxf(lm, x[j]);
+            if (__ballot(lm > m[q] + kLazyMargin)) {
+                float bm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
+                bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+                const float mn = fmaxf(m[q], bm);
+                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[q] - mn);
+                lpart[q] *= alpha;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) acc[q][u] *= alpha;
+                m[q] = mn;
+            }
+            const float mref = m[q] == -INFINITY ? 0.f : m[q];
+            uint32_t pb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pb[j] = f32_to_bf16(__builtin_amdgcn_exp2f(x[j] - mref));
+                lpart[q] += __uint_as_float(pb[j] << 16);
+            }
+            const bf16x8 pv = __builtin_bit_cast(
+                bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                              pb[6] | (pb[7] << 16)});
+#pragma unroll
+            for (int u = 0; u < DT; ++u)
+                acc[q][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[u], pv, acc[q][u], 0, 0, 0);
+        }
+    }
+
+    // every wave finishes its own tiles: lane holds O^T[dim 16u+4g+j][row] in
+    // acc[q][u][j], its row's m, and a quarter of its row's sum
+#pragma unroll
+    for (int q = 0; q < QTW; ++q) {
+        if (!tile_ok[q]) continue;
+        float l = lpart[q] + __shfl_xor(lpart[q], 16, kWave);
+        l += __shfl_xor(l, 32, kWave);
+        const int qt = (qg * kWavesPerGroup + wave) * QTW + q;
+        const long long slot = (((long long)b * a.Hkv + kvh) * a.nsplit + sp) * a.nq + qt;
+        const size_t prow = (size_t)slot * 16 + c;
+        if constexpr (kDirect) {
+            if (row_ok[q]) {
+                const float inv = l > 0.f ? 1.0f / l : 0.f;
+                float* orow = a.out + (((size_t)b * a.T + t[q]) * a.Hq + h[q]) * DH + 4 * g;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4v*>(orow + 16 * u) = acc[q][u] * inv;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < DT; ++u)
+                *reinterpret_cast<f32x4v*>(a.part_o + prow * DH + 16 * u + 4 * g) = acc[q][u];
+            if (g == 0) {
+                a.part_ml[2 * prow] = m[q];
+                a.part_ml[2 * prow + 1] = l;
+            }
+        }
+    }
+}
+
 // Merge the context splits of every query row, in split order:
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
 template <int DH>
@@ -478,11 +699,28 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
         if (p.qt == 1) SV_ATTN(64, DIRECT, 1);                                              \
         else if (p.qt == 2) SV_ATTN(64, DIRECT, 2);                                         \
         else SV_ATTN(64, DIRECT, 4);
-        if (head_dim == 128) {
+#define SV_RING(DH, DIRECT, QTW)                                                            \
+        SV_LAUNCH(prof, (attn_ring_kernel<DH, DIRECT, QTW>), grid, kWavesPerGroup * kWave, stream, a)
+#define SV_RING_128(DIRECT)                                                                 \
+        if (p.qt == 1) SV_RING(128, DIRECT, 1); else SV_RING(128, DIRECT, 2);
+#define SV_RING_64(DIRECT)                                                                  \
+        if (p.qt == 1) SV_RING(64, DIRECT, 1);                                              \
+        else if (p.qt == 2) SV_RING(64, DIRECT, 2);                                         \
+        else SV_RING(64, DIRECT, 4);
+        if (p.ring) {
+            if (head_dim == 128) {
+                if (p.nsplit > 1) { SV_RING_128(false) } else { SV_RING_128(true) }
+            } else {
+                if (p.nsplit > 1) { SV_RING_64(false) } else { SV_RING_64(true) }
+            }
+        } else if (head_dim == 128) {
             if (p.nsplit > 1) { SV_ATTN_128(false) } else { SV_ATTN_128(true) }
         } else {
             if (p.nsplit > 1) { SV_ATTN_64(false) } else { SV_ATTN_64(true) }
         }
+#undef SV_RING_64
+#undef SV_RING_128
+#undef SV_RING
 #undef SV_ATTN_64
 #undef SV_ATTN_128
 #undef SV_ATTN

@@ -62,8 +62,10 @@ CASES = [
     (4, 5, 64, 8, 128, [1000, 2000, 1, 64], 64), # 70B-shaped heads, split context
     (1, 2, 4, 4, 64, [4000], 126),               # long context, G = 1
     (5, 1, 12, 4, 128, [10, 20, 30, 40, 50], 2), # T = 1 (no drafts)
-    (2, 16, 8, 1, 64, [300, 50], 12),            # 128 rows per KV head: two groups of 4 tiles
-    (1, 16, 64, 8, 128, [700], 24),              # 70B-shaped heads, K = 15: 4 groups of 2 tiles, split
+    (2, 16, 8, 1, 64, [300, 50], 12),            # 128 rows per KV head: 8 tiles (ring)
+    (1, 16, 64, 8, 128, [700], 24),              # 70B-shaped heads, K = 15: 8 tiles, split
+    (2, 8, 8, 1, 128, [64, 500], 18),            # 4 tiles: the LDS-ring kernel, one tile per wave
+    (1, 16, 16, 1, 64, [200], 8),                # 16 tiles: ring, four tiles per wave
 ]
 
 

@@ -230,15 +230,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QT == 1 ? 2 : 1) void attn_
                 m[i] = mn;
             }
             const float mref = m[i] == -INFINITY ? 0.f : m[i];   // no visible key yet: p = 0
-            uint32_t pb[8];
+            uint32_t pw[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pb[j] = f32_to_bf16(__builtin_amdgcn_exp2f(x[j] - mref));
-                lpart[i] += __uint_as_float(pb[j] << 16);
+            for (int j = 0; j < 4; ++j) {
+                pw[j] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * j] - mref),
+                                    __builtin_amdgcn_exp2f(x[2 * j + 1] - mref));
+                lpart[i] += bf16lo(pw[j]);     // in key order, as the product sums them
+                lpart[i] += bf16hi(pw[j]);
             }
-            const bf16x8 pv = __builtin_bit_cast(
-                bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                              pb[6] | (pb[7] << 16)});
+            const bf16x8 pv = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
             for (int u = 0; u < DT; ++u)
                 acc[i][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.v[u], pv, acc[i][u], 0, 0, 0);
@@ -487,15 +487,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QTW <= 2 ? 2 : 1) void attn
                 m[q] = mn;
             }
             const float mref = m[q] == -INFINITY ? 0.f : m[q];
-            uint32_t pb[8];
+            uint32_t pw[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pb[j] = f32_to_bf16(__builtin_amdgcn_exp2f(x[j] - mref));
-                lpart[q] += __uint_as_float(pb[j] << 16);
+            for (int j = 0; j < 4; ++j) {
+                pw[j] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * j] - mref),
+                                    __builtin_amdgcn_exp2f(x[2 * j + 1] - mref));
+                lpart[q] += bf16lo(pw[j]);     // in key order, as the product sums them
+                lpart[q] += bf16hi(pw[j]);
             }
-            const bf16x8 pv = __builtin_bit_cast(
-                bf16x8, u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                              pb[6] | (pb[7] << 16)});
+            const bf16x8 pv = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
             for (int u = 0; u < DT; ++u)
                 acc[q][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[u], pv, acc[q][u], 0, 0, 0);

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(WN * WM * kWave, WPE) void mfma_tiled_kernel(
                 const size_t o = ((size_t)(m >> 4) * (N >> 5) + (n >> 5)) * 512 +
                                  ((m & 15) + 16 * ((n & 31) >> 3)) * 8 + (n & 7);
                 uint2 pk;
-                pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
-                pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
+                pk.x = pack_bf16x2(silu(v[0]), silu(v[1]));
+                pk.y = pack_bf16x2(silu(v[2]), silu(v[3]));
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = pk;
                 continue;
             }

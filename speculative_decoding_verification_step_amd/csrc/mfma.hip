@@ -182,8 +182,8 @@ __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
                                        : o);
                 if (kActT || (vec && n0 + 3 < N)) {
                     uint2 pk;
-                    pk.x = f32_to_bf16(silu(v[0])) | (f32_to_bf16(silu(v[1])) << 16);
-                    pk.y = f32_to_bf16(silu(v[2])) | (f32_to_bf16(silu(v[3])) << 16);
+                    pk.x = pack_bf16x2(silu(v[0]), silu(v[1]));
+                    pk.y = pack_bf16x2(silu(v[2]), silu(v[3]));
                     *reinterpret_cast<uint2*>(dst) = pk;
                 } else {
 #pragma unroll

@@ -143,8 +143,8 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
                          h[v].z * inv_rms * gv.z, h[v].w * inv_rms * gv.w};
         if constexpr (kBf16) {
             uint2 packed;
-            packed.x = f32_to_bf16(y.x) | (f32_to_bf16(y.y) << 16);
-            packed.y = f32_to_bf16(y.z) | (f32_to_bf16(y.w) << 16);
+            packed.x = pack_bf16x2(y.x, y.y);
+            packed.y = pack_bf16x2(y.z, y.w);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(act) + act_off(c)) = packed;
         } else {
             reinterpret_cast<f32x4*>(static_cast<float*>(act) + off)[c] = y;

@@ -109,6 +109,16 @@ struct AttnArgs {
 
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
+// Entry kb of a request's block-table row (row and kb the same for the whole
+// wave).  The table is read-only while attention runs, so the lookup goes
+// through the constant address space: a scalar load, counted on lgkmcnt.  As
+// a vector load its wait (vmcnt, which retires in order) would also wait for
+// every K/V copy issued before it, taking the prefetch depth away.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int table_entry(const int32_t* row, int kb) {
+    return ((const const_i32*)row)[__builtin_amdgcn_readfirstlane(kb)];
+}
+
 template <int DH>
 struct KVRegs {
     bf16x8 k0[DH / 32], k1[DH / 32], v[DH / 16];
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QT == 1 ? 2 : 1) void attn_
 
     const int32_t* trow = a.table + (size_t)b * a.max_blocks;
     auto load = [&](KVRegs<DH>& kv, int kb) {
-        int blk = trow[kb];
+        int blk = table_entry(trow, kb);
         blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
         const uint16_t* kbase = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlk * DH;
         const uint16_t* vbase = a.vc + ((size_t)blk * a.Hkv + kvh) * DH * kBlk;
@@ -410,8 +420,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QTW <= 2 ? 2 : 1) void attn
     const int32_t* trow = a.table + (size_t)b * a.max_blocks;
     const int vrow_c = lane >> 2;                              // V chunk copy: tile row
     const int vchunk = (lane & 3) ^ ((vrow_c >> 2) & 3);       // ... and its swizzled chunk
-    auto issue = [&](int kb, int st) {
-        int blk = trow[kb];
+    auto issue = [&](int blk, int st) {
         blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
         const uint16_t* kbase = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlk * DH;
         const uint16_t* vbase = a.vc + ((size_t)blk * a.Hkv + kvh) * DH * kBlk;
@@ -432,7 +441,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QTW <= 2 ? 2 : 1) void attn
 
 #pragma unroll
     for (int p = 0; p < kRingStages - 1; ++p)
-        if (p < nblk) issue(kb0 + p, p);
+        if (p < nblk) issue(table_entry(trow, kb0 + p), p);
+    // the id of the next block to copy is read one block ahead, so its
+    // scalar load has landed by the time the copy is issued
+    int next_blk = kRingStages - 1 < nblk ? table_entry(trow, kb0 + kRingStages - 1) : 0;
     const int sw = (c >> 2) & 3;
     for (int i = 0; i < nblk; ++i) {
         // this wave's copies of block i are done once at most kRingStages - 2
@@ -441,7 +453,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QTW <= 2 ? 2 : 1) void attn
         if (i + kRingStages - 2 < nblk) wait_vmcnt<PER_WAVE * (kRingStages - 2)>();
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        if (i + kRingStages - 1 < nblk) issue(kb0 + i + kRingStages - 1, (i + kRingStages - 1) % kRingStages);
+        if (i + kRingStages - 1 < nblk) {
+            issue(next_blk, (i + kRingStages - 1) % kRingStages);
+            if (i + kRingStages < nblk) next_blk = table_entry(trow, kb0 + i + kRingStages);
+        }
         const uint16_t* stage = ring[i % kRingStages];
         bf16x8 k0[KS], k1[KS], v[DT];
 #pragma unroll

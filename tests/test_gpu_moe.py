@@ -42,7 +42,7 @@ def _check(sv, w, model, M, sub):
 
 
 @gpu
-@pytest.mark.parametrize("M", [1, 5, 17, 64, 100, 300])
+@pytest.mark.parametrize("M", [1, 5, 9, 12, 16, 17, 64, 65, 100, 300])
 def test_small_moe_forward(M):
     sv = require_gpu()
     # several weight fragments, a ragged vocabulary, experts idle and busy

@@ -334,16 +334,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QT == 1 ? 2 : 1) void attn_
 }
 
 
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
 // From 4 query tiles per KV head: the four waves own QTW tiles each (4 * QTW
 // tiles = up to 128 query rows per workgroup) and walk the SAME blocks of the
 // context range, which pass once through a ring of kRingStages LDS stages

@@ -36,6 +36,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
+// ---- copies into LDS ----------------------------------------------------------
+// LDS pointers for __builtin_amdgcn_global_load_lds (one 16-byte piece per
+// lane, written lane-contiguously at the wave-uniform LDS address).  Those
+// copies are counted on vmcnt like any vector load, and the compiler does not
+// wait for them before reading the LDS they fill: the kernels wait explicitly.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ---- activation functions ---------------------------------------------------
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
 

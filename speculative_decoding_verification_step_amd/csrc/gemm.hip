@@ -31,15 +31,6 @@ namespace sv {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 template <int WN, int WM, int FN, int FM, int NS, int WPE, int EPI>
 __global__ __launch_bounds__(WN * WM * kWave, WPE) void mfma_tiled_kernel(

@@ -33,12 +33,84 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// Fixed-order sum of a workgroup's NKS k slices through LDS (`red`, NKS x NR
+// x MF x 64 x 16 bytes), one weight fragment of every row group at a time,
+// and the epilogue.  Each wave stores its accumulators lane-major (one
+// 16-byte write per lane and fragment); each task then sums the NKS copies of
+// one lane's four outputs (16-byte reads, no bank conflicts) and writes four
+// consecutive outputs n0..n0+3 of one row m: the lane's rows of the MFMA
+// result tile.  Fragment rf of row group rr holds outputs n = 16 ((blk NR +
+// rr) RF + rf) + 0..15.
+template <int MF, int RF, int NR, int NKS, int EPI, bool kActT>
+__device__ __forceinline__ void reduce_store(const f32x4v (&acc)[RF][MF],
+                                             f32x4v (*red)[NR][MF][kWave], int ks, int rg,
+                                             int lane, int blk, int M, int N,
+                                             void* __restrict__ out, size_t split_stride) {
+    constexpr int NWK = NR * NKS;
+    float* plane = static_cast<float*>(out) + (size_t)blockIdx.y * split_stride;
+    // rows start 16-byte aligned (8 for bf16 outputs)
+    const bool vec = (N & 3) == 0 && ((uintptr_t)out & (EPI == kEpiSilu ? 7 : 15)) == 0;
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) {
+        if (rf) __syncthreads();        // the previous fragment's readers are done
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) red[ks][rg][mf][lane] = acc[rf][mf];
+        __syncthreads();
+        constexpr int kTasks = NR * MF * kWave;
+        for (int e = threadIdx.x; e < kTasks; e += NWK * kWave) {
+            const int l = e % kWave;
+            const int mf = (e / kWave) % MF;
+            const int rr = e / (kWave * MF);
+            const int n0 = ((blk * NR + rr) * RF + rf) * 16 + 4 * (l >> 4);
+            const int m = mf * 16 + (l & 15);
+            if (n0 >= N || m >= M) continue;
+            f32x4v v = red[0][rr][mf][l];
+#pragma unroll
+            for (int w = 1; w < NKS; ++w) v += red[w][rr][mf][l];
+            const size_t o = (size_t)m * N + n0;
+            if constexpr (EPI == kEpiSilu) {
+                // the next projection's activations, row-major or in the
+                // operand layout (N % 32 == 0: n0..n0+3 are 8 contiguous bytes
+                // of one block)
+                uint16_t* dst = static_cast<uint16_t*>(out) +
+                                (kActT ? ((size_t)(m >> 4) * (N >> 5) + (n0 >> 5)) * 512 +
+                                             ((m & 15) + 16 * ((n0 & 31) >> 3)) * 8 + (n0 & 7)
+                                       : o);
+                if (kActT || (vec && n0 + 3 < N)) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(silu(v[0]), silu(v[1]));
+                    pk.y = pack_bf16x2(silu(v[2]), silu(v[3]));
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n0 + r < N) dst[r] = (uint16_t)f32_to_bf16(silu(v[r]));
+                }
+                continue;
+            }
+            float* dst = EPI == kEpiResidual && split_stride ? plane + o : static_cast<float*>(out) + o;
+            if (vec && n0 + 3 < N) {
+                if constexpr (EPI == kEpiResidual)
+                    if (!split_stride) v += *reinterpret_cast<const f32x4v*>(dst);   // one owner per element
+                *reinterpret_cast<f32x4v*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (n0 + r >= N) break;
+                    if constexpr (EPI == kEpiResidual)
+                        if (!split_stride) { dst[r] += v[r]; continue; }
+                    dst[r] = v[r];
+                }
+            }
+        }
+    }
+}
+
 template <int MF, int RF, int NR, int NKS, int U, int EPI, bool kTiled, bool kActT>
 __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ act, int M, int N, int K,
     int steps_per_split, void* __restrict__ out, size_t split_stride) {
     static_assert(NKS >= 2, "the k slices are reduced through LDS");
-    constexpr int NWK = NR * NKS;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int rg = wave % NR;           // row group of this wave
@@ -144,70 +216,9 @@ __global__ __launch_bounds__(NR * NKS * kWave) void mfma_skinny_kernel(
         compute(wb, xb);
     }
 
-    // fixed-order reduction of the NKS k slices through LDS, one weight
-    // fragment of every row group at a time.  Each wave stores its
-    // accumulators lane-major (one 16-byte write per lane and fragment); each
-    // task then sums the NKS copies of one lane's four outputs (16-byte
-    // reads, no bank conflicts) and writes four consecutive outputs n0..n0+3
-    // of one row m: the lane's rows of the MFMA result tile.
     __shared__ f32x4v red[NKS][NR][MF][kWave];
-    float* plane = static_cast<float*>(out) + (size_t)blockIdx.y * split_stride;
-    // rows start 16-byte aligned (8 for bf16 outputs)
-    const bool vec = (N & 3) == 0 && ((uintptr_t)out & (EPI == kEpiSilu ? 7 : 15)) == 0;
-#pragma unroll
-    for (int rf = 0; rf < RF; ++rf) {
-        if (rf) __syncthreads();        // the previous fragment's readers are done
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) red[ks][rg][mf][lane] = acc[rf][mf];
-        __syncthreads();
-        constexpr int kTasks = NR * MF * kWave;
-        for (int e = threadIdx.x; e < kTasks; e += NWK * kWave) {
-            const int l = e % kWave;
-            const int mf = (e / kWave) % MF;
-            const int rr = e / (kWave * MF);
-            const int n0 = ((blockIdx.x * NR + rr) * RF + rf) * 16 + 4 * (l >> 4);
-            const int m = mf * 16 + (l & 15);
-            if (n0 >= N || m >= M) continue;
-            f32x4v v = red[0][rr][mf][l];
-#pragma unroll
-            for (int w = 1; w < NKS; ++w) v += red[w][rr][mf][l];
-            const size_t o = (size_t)m * N + n0;
-            if constexpr (EPI == kEpiSilu) {
-                // the next projection's activations, row-major or in the
-                // operand layout (N % 32 == 0: n0..n0+3 are 8 contiguous bytes
-                // of one block)
-                uint16_t* dst = static_cast<uint16_t*>(out) +
-                                (kActT ? ((size_t)(m >> 4) * (N >> 5) + (n0 >> 5)) * 512 +
-                                             ((m & 15) + 16 * ((n0 & 31) >> 3)) * 8 + (n0 & 7)
-                                       : o);
-                if (kActT || (vec && n0 + 3 < N)) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(silu(v[0]), silu(v[1]));
-                    pk.y = pack_bf16x2(silu(v[2]), silu(v[3]));
-                    *reinterpret_cast<uint2*>(dst) = pk;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n0 + r < N) dst[r] = (uint16_t)f32_to_bf16(silu(v[r]));
-                }
-                continue;
-            }
-            float* dst = EPI == kEpiResidual && split_stride ? plane + o : static_cast<float*>(out) + o;
-            if (vec && n0 + 3 < N) {
-                if constexpr (EPI == kEpiResidual)
-                    if (!split_stride) v += *reinterpret_cast<const f32x4v*>(dst);   // one owner per element
-                *reinterpret_cast<f32x4v*>(dst) = v;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (n0 + r >= N) break;
-                    if constexpr (EPI == kEpiResidual)
-                        if (!split_stride) { dst[r] += v[r]; continue; }
-                    dst[r] = v[r];
-                }
-            }
-        }
-    }
+    reduce_store<MF, RF, NR, NKS, EPI, kActT>(acc, red, ks, rg, lane, blockIdx.x, M, N, out,
+                                              split_stride);
 }
 
 template <int MF, int RF, int NR, int NKS, int U, int EPI, bool kActT = false>

@@ -213,11 +213,13 @@ __device__ __forceinline__ void topk_rows(const float* zs, int rows, int E, int 
 // expert's rows is therefore not fixed, and nothing depends on it: every
 // output row of the grouped kernels is its own dot products, and the fold
 // finds each pair's row through inv.  Also lists the experts with rows in
-// id order (alist[0 .. *nact - 1]) for the grouped kernels.  cnt, loff: LDS
-// [E] and [E + 1].
+// id order (alist[0 .. *nact - 1]) for the grouped kernels.  With `pad`
+// every expert's range is rounded up to a multiple of 16 rows (offs and inv
+// count padded rows) and the padding rows get perm = -1.  cnt, loff: LDS [E]
+// and [E + 1].
 template <int THREADS>
-__device__ __forceinline__ void sort_pairs(const int32_t* lsel, int M, int E, int k, int32_t* cnt,
-                                           int32_t* loff, int32_t* __restrict__ offs,
+__device__ __forceinline__ void sort_pairs(const int32_t* lsel, int M, int E, int k, int pad,
+                                           int32_t* cnt, int32_t* loff, int32_t* __restrict__ offs,
                                            int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                            int32_t* __restrict__ alist, int32_t* __restrict__ nact,
                                            int32_t* __restrict__ active) {
@@ -233,8 +235,9 @@ __device__ __forceinline__ void sort_pairs(const int32_t* lsel, int M, int E, in
         for (int q = 0; q < Q; ++q) {
             const int x = Q * tid + q;
             c[q] = x < E ? cnt[x] : 0;
-            tot += c[q];
             nz += c[q] > 0;
+            if (pad) c[q] = (c[q] + 15) & ~15;
+            tot += c[q];
         }
         int itot = tot, inz = nz;            // inclusive scans across lanes
 #pragma unroll
@@ -266,6 +269,8 @@ __device__ __forceinline__ void sort_pairs(const int32_t* lsel, int M, int E, in
         offs[x] = loff[x];
         if (x < E) cnt[x] = loff[x];         // next free row of expert x
     }
+    if (pad)
+        for (int r = tid; r < loff[E]; r += THREADS) perm[r] = -1;
     __syncthreads();
     for (int i = tid; i < n; i += THREADS) {
         const int pos = atomicAdd(&cnt[lsel[i]], 1);
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
 }
 
 __global__ __launch_bounds__(kRouteThreads) void moe_sort_kernel(
-    const int32_t* __restrict__ sel, int M, int E, int k, int32_t* __restrict__ offs,
+    const int32_t* __restrict__ sel, int M, int E, int k, int pad, int32_t* __restrict__ offs,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ alist,
     int32_t* __restrict__ nact, int32_t* __restrict__ active) {
     __shared__ int32_t lsel[kMoeMaxRows * kMoeMaxTopK];
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_sort_kernel(
     __shared__ int32_t loff[kMoeMaxExperts + 1];
     for (int i = threadIdx.x; i < M * k; i += kRouteThreads) lsel[i] = sel[i];
     __syncthreads();
-    sort_pairs<kRouteThreads>(lsel, M, E, k, cnt, loff, offs, perm, inv, alist, nact, active);
+    sort_pairs<kRouteThreads>(lsel, M, E, k, pad, cnt, loff, offs, perm, inv, alist, nact, active);
 }
 
 // ---- grouped matmul -------------------------------------------------------------
@@ -318,7 +323,12 @@ __global__ __launch_bounds__(kRouteThreads) void moe_sort_kernel(
 // read, and runs MF 16-row activation fragments per pass over the expert's
 // rows through them (one activation load serves RF weight fragments;
 // fragments past the expert's rows are skipped by the whole wave).
-template <int EPI, int MF, int U, int RF>
+// Padded rows (offs multiples of 16, perm = -1 on an expert's padding
+// rows, which read as zeros): kActIn - `act` is in the operand layout (one
+// KiB per 16 rows x 32 k), so an activation load is a wave-uniform base plus
+// a lane offset and no row index is read; kActOut - the SiLU output is
+// written in that layout for the down projection.
+template <int EPI, int MF, int U, int RF, bool kActIn, bool kActOut>
 __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
     const uint16_t* __restrict__ W, size_t wstride, int N, int K, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ perm, int gather, int top_k, const int32_t* __restrict__ offs,
@@ -356,23 +366,37 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
 
     for (int pass = 0; pass < rows; pass += 16 * MF) {
         const int prow = rows - pass;      // rows left, > 0
-        const uint16_t* arow[MF];
+        const uint16_t* arow[kActIn ? 1 : MF];
         bool aval[MF];
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) {
-            const int j = pass + mf * 16 + r16;
-            aval[mf] = j < rows;
-            const int rr = row0 + (aval[mf] ? j : 0);
-            const int src = gather ? perm[rr] / top_k : rr;
-            arow[mf] = act + (size_t)src * K + 8 * g;
+            if constexpr (kActIn) {
+                aval[mf] = mf * 16 < prow;
+            } else {
+                const int j = pass + mf * 16 + r16;
+                aval[mf] = j < rows;
+                const int rr = row0 + (aval[mf] ? j : 0);
+                int src = rr;
+                if (gather) {
+                    const int pi = perm[rr];
+                    aval[mf] = aval[mf] && pi >= 0;
+                    src = pi >= 0 ? pi / top_k : 0;
+                }
+                arow[mf] = act + (size_t)src * K + 8 * g;
+            }
         }
+        // operand layout: the KiB of row block mf at step s lies (mf S + s)
+        // KiB past the pass's first block
+        const char* ablk = reinterpret_cast<const char*>(act) + (size_t)((row0 + pass) >> 4) * S * 1024;
         auto loadx = [&](bf16x8 (&x)[U][MF], int s) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int mf = 0; mf < MF; ++mf)
                     x[u][mf] = (s + u < s1 && aval[mf])
-                                   ? *reinterpret_cast<const bf16x8*>(arow[mf] + 32 * (s + u))
+                                   ? *reinterpret_cast<const bf16x8*>(
+                                         kActIn ? ablk + (uint32_t)(lane * 16 + (mf * S + s + u) * 1024)
+                                                : reinterpret_cast<const char*>(arow[kActIn ? 0 : mf] + 32 * (s + u)))
                                    : zero8;
         };
         f32x4v acc[RF][MF];
@@ -422,8 +446,13 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
             const size_t o = (size_t)(row0 + j) * N + n0;
             const bool full = (N & 3) == 0 && n0 + 3 < N;   // rows start 16-byte aligned
             if constexpr (EPI == kEpiSilu) {
-                uint16_t* dst = static_cast<uint16_t*>(out) + o;
-                if (full) {
+                // kActOut: the down projection's operand layout (N % 32 == 0)
+                const int pr = row0 + j;
+                uint16_t* dst = static_cast<uint16_t*>(out) +
+                                (kActOut ? ((size_t)(pr >> 4) * (N >> 5) + (n0 >> 5)) * 512 +
+                                               ((pr & 15) + 16 * ((n0 & 31) >> 3)) * 8 + (n0 & 7)
+                                         : o);
+                if (kActOut || full) {
                     uint2 pk;
                     pk.x = pack_bf16x2(silu(v[0]), silu(v[1]));
                     pk.y = pack_bf16x2(silu(v[2]), silu(v[3]));
@@ -451,10 +480,17 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
 constexpr size_t kAlign = 256;
 size_t aup(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Mean rows per expert (M top_k / E) from which each expert's rows are
+// padded to 16 and the up projection writes its SiLU output in the operand
+// layout, which the down projection then reads as one KiB per 16 rows x 32 k.
+constexpr int kMoeActTiledMeanRows = 20;
+
 struct MoePlan {
+    int act_tiled = 0;         // padded rows, operand-layout up-projection output
     int head_kind = kMfmaSkinny;
     int head_act_tiled = 0;    // the last norm writes the head's activations in the operand layout
     int router_spw = 0, router_splits = 0;   // reduction steps per router split, splits
+    size_t rows = 0;           // sorted rows (padded: M top_k + 15 per listed expert at most)
     size_t off_h, off_a, off_part, off_sel, off_w, off_offs, off_list, off_perm, off_inv, off_s,
         off_y, bytes;
 };
@@ -462,6 +498,9 @@ struct MoePlan {
 MoePlan plan_moe(const sv_moe_desc& d, int M) {
     MoePlan p{};
     const size_t Mk = (size_t)M * d.top_k;
+    const size_t listed = (size_t)d.n_experts < Mk ? (size_t)d.n_experts : Mk;
+    p.act_tiled = (M * d.top_k + d.n_experts - 1) / d.n_experts >= kMoeActTiledMeanRows;
+    p.rows = p.act_tiled ? Mk + 15 * listed : Mk;
     p.head_kind = M >= kHeadTiledMinRows ? kMfmaTiled : kMfmaSkinny;
     p.head_act_tiled = M >= kActTiledMinRows;
     const int S = d.d / 32;
@@ -476,10 +515,10 @@ MoePlan plan_moe(const sv_moe_desc& d, int M) {
     p.off_w = o; o = aup(o + Mk * 4);
     p.off_offs = o; o = aup(o + (size_t)(d.n_experts + 2) * 4);   // offsets, then the count
     p.off_list = o; o = aup(o + (size_t)d.n_experts * 4);
-    p.off_perm = o; o = aup(o + Mk * 4);
+    p.off_perm = o; o = aup(o + p.rows * 4);
     p.off_inv = o; o = aup(o + Mk * 4);
-    p.off_s = o; o = aup(o + Mk * d.ffn * 2);
-    p.off_y = o; o = aup(o + Mk * d.d * 4);
+    p.off_s = o; o = aup(o + p.rows * d.ffn * 2);
+    p.off_y = o; o = aup(o + p.rows * d.d * 4);
     p.bytes = o;
     return p;
 }
@@ -492,13 +531,13 @@ int moe_hip_fail(hipError_t e, const char* what) {
 // on average (M * top_k / E): few rows want many workgroups and deep weight
 // buffers; many rows want each activation load shared by several weight
 // fragments (measured on the 64-expert top-6 workload over M = 1 .. 576).
-template <int EPI>
+template <int EPI, bool kActIn, bool kActOut>
 void launch_grouped(ProfScope& prof, int M, int E, int k, int listed, int nfrag, hipStream_t s,
                     const uint16_t* W, size_t wstride, int N, int K, const uint16_t* act,
                     const int32_t* perm, int gather, const int32_t* offs, const int32_t* alist,
                     const int32_t* nact, void* out) {
 #define SV_GROUPED(MF, U, RF)                                                                      \
-    SV_LAUNCH(prof, (moe_grouped_kernel<EPI, MF, U, RF>),                                         \
+    SV_LAUNCH(prof, (moe_grouped_kernel<EPI, MF, U, RF, kActIn, kActOut>),                        \
               (unsigned)(listed * ((nfrag + RF - 1) / RF)), kGroupWaves * kWave, s, W, wstride, N, \
               K, act, perm, gather, k, offs, alist, nact, out)
     const int mean_rows = (M * k + E - 1) / E;
@@ -607,8 +646,8 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
         }
         {
             ProfScope prof("moe_sort", s, (double)M * k * 12, 0.0);
-            SV_LAUNCH(prof, moe_sort_kernel, 1, kRouteThreads, s, sel, M, E, k, offs, perm, inv,
-                      alist, nact, act_out);
+            SV_LAUNCH(prof, moe_sort_kernel, 1, kRouteThreads, s, sel, M, E, k, p.act_tiled, offs,
+                      perm, inv, alist, nact, act_out);
             e = hipGetLastError();
             if (e != hipSuccess) return moe_hip_fail(e, "sort launch");
         }
@@ -616,20 +655,33 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
         {
             // bytes depend on the experts the device picks: counted by the caller
             ProfScope prof("moe_up_silu", s, 0.0, 2.0 * M * k * (double)d.ffn * d.d);
-            launch_grouped<kEpiSilu>(prof, M, E, k, listed, (d.ffn + 15) / 16, s,
-                                     static_cast<const uint16_t*>(d.w_up) + (size_t)l * E * up_stride,
-                                     up_stride, d.ffn, d.d, static_cast<const uint16_t*>(a), perm, 1,
-                                     offs, alist, nact, S);
+            const uint16_t* wu = static_cast<const uint16_t*>(d.w_up) + (size_t)l * E * up_stride;
+            if (p.act_tiled)
+                launch_grouped<kEpiSilu, false, true>(prof, M, E, k, listed, (d.ffn + 15) / 16, s, wu,
+                                                      up_stride, d.ffn, d.d,
+                                                      static_cast<const uint16_t*>(a), perm, 1, offs,
+                                                      alist, nact, S);
+            else
+                launch_grouped<kEpiSilu, false, false>(prof, M, E, k, listed, (d.ffn + 15) / 16, s,
+                                                       wu, up_stride, d.ffn, d.d,
+                                                       static_cast<const uint16_t*>(a), perm, 1, offs,
+                                                       alist, nact, S);
             e = hipGetLastError();
             if (e != hipSuccess) return moe_hip_fail(e, "grouped up launch");
         }
         {
             ProfScope prof("moe_down", s, 0.0, 2.0 * M * k * (double)d.ffn * d.d);
-            launch_grouped<kEpiStore>(prof, M, E, k, listed, (d.d + 15) / 16, s,
-                                      static_cast<const uint16_t*>(d.w_down) +
-                                          (size_t)l * E * down_stride,
-                                      down_stride, d.d, d.ffn, static_cast<const uint16_t*>(S), perm,
-                                      0, offs, alist, nact, Y);
+            const uint16_t* wd = static_cast<const uint16_t*>(d.w_down) + (size_t)l * E * down_stride;
+            if (p.act_tiled)
+                launch_grouped<kEpiStore, true, false>(prof, M, E, k, listed, (d.d + 15) / 16, s, wd,
+                                                down_stride, d.d, d.ffn,
+                                                static_cast<const uint16_t*>(S), perm, 0, offs, alist,
+                                                nact, Y);
+            else
+                launch_grouped<kEpiStore, false, false>(prof, M, E, k, listed, (d.d + 15) / 16, s, wd,
+                                                 down_stride, d.d, d.ffn,
+                                                 static_cast<const uint16_t*>(S), perm, 0, offs, alist,
+                                                 nact, Y);
             e = hipGetLastError();
             if (e != hipSuccess) return moe_hip_fail(e, "grouped down launch");
         }

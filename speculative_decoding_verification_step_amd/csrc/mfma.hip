@@ -242,6 +242,31 @@ hipError_t launch_shape(const MatmulArgs& a, const uint16_t* act, void* out, int
     return hipGetLastError();
 }
 
+// 17..48 rows of a wide projection (operand-layout activations): eight
+// weight fragments per wave halve the activation loads per weight byte, when
+// the grid still fills the chip.  Up projection (no K split): N >= 24576
+// rows, 192+ workgroups.  Down projection: a K split that gives 256
+// workgroups of 128 rows must still leave every wave 16+ steps.  Measured on
+// the 70B-layer share at 40 rows: up 88 -> 79 us, down 83 -> 79 us; with
+// 112 workgroups (8B-shaped up) or 7 steps per wave (8B-shaped down) eight
+// fragments were 40% and 7% slower.
+constexpr int kWideMinRows = 17, kWideMaxRows = 48;
+
+// K split of a wide down projection (0: not wide)
+int wide_down_splits(int N, int K) {
+    const long long wg = (N + 127) / 128;
+    int ksg = 1;
+    while (wg * ksg < 256 && ksg < 8) ksg *= 2;
+    return wg * ksg >= 256 && (K / 32) / (ksg * 8) >= 16 ? ksg : 0;
+}
+
+bool skinny_wide(int M, int N, int K, int epi) {
+    if (M < kWideMinRows || M > kWideMaxRows) return false;
+    if (epi == kEpiSilu) return N >= 24576;
+    if (epi == kEpiResidual) return wide_down_splits(N, K) > 0;
+    return false;
+}
+
 template <int MF, int EPI>
 hipError_t launch_mf(const MatmulArgs& a, const uint16_t* act, void* out, int Mc, int ksg,
                      size_t stride, hipStream_t stream) {
@@ -252,6 +277,10 @@ hipError_t launch_mf(const MatmulArgs& a, const uint16_t* act, void* out, int Mc
         // a vocabulary of 400+ 256-row groups); the rest four fragments per
         // wave and eight k slices (two-step buffers up to 64 rows, one above).
         if (!a.tiled) return hipErrorInvalidValue;
+        if constexpr (EPI != kEpiStore && MF >= 2 && MF <= 3) {
+            if (skinny_wide(a.M, a.N, a.K, EPI))
+                return launch_shape<MF, 8, 1, 8, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
+        }
         if constexpr (EPI == kEpiStore && MF >= 2 && MF <= 4) {
             if ((a.N + 255) / 256 >= 400)
                 return launch_shape<MF, 8, 2, 2, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
@@ -313,6 +342,10 @@ int skinny_splits(int M, int N, int K, int tiled, int act_tiled) {
     // projection has few workgroups: split K until the grid fills 256 CUs
     // (>= 16 steps of 32 per split half, so every k slice keeps a few steps)
     if (!tiled || (M <= 16 && !act_tiled)) return 0;
+    if (act_tiled && skinny_wide(M, N, K, kEpiResidual)) {
+        const int ksg = wide_down_splits(N, K);
+        return ksg > 1 ? ksg : 0;
+    }
     const long long wg = (N + (act_tiled ? 63 : 127)) / (act_tiled ? 64 : 128);
     int ksg = 1;
     while (wg * ksg < 256 && ksg < 8 && (K / 32) / (ksg * 2) >= 16) ksg *= 2;

@@ -69,6 +69,37 @@ def test_wide_projections_ragged_fragments(M):
 
 
 @gpu
+@pytest.mark.parametrize("M", [17, 33, 48])
+def test_wide_up_eight_fragments_ragged(M):
+    """17..48 rows on an up projection of 24576+ outputs run eight weight
+    fragments per wave: ffn 24640 = 1540 fragments, so the last workgroup
+    holds four and skips four."""
+    sv = require_gpu()
+    w = workload.Workload("wide-up-bf16", 256, 24640, 1, 1001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 5)
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w, M, sub=M)
+    z = cpu(m.forward(torch.from_numpy(h).cuda()))
+    _check(z, of.forward(model, h), TOL_BF16, f"wide up M={M}")
+
+
+@gpu
+@pytest.mark.parametrize("M", [20, 48])
+def test_wide_down_eight_fragments_split(M):
+    """A down projection with d = 4096 outputs and a 32768-long reduction at
+    17..48 rows: eight weight fragments per wave and a K split of 8 partial
+    planes (32 x 8 = 256 workgroups, 16 steps per wave); its up projection
+    (32768 outputs) runs eight fragments too."""
+    sv = require_gpu()
+    w = workload.Workload("wide-down-bf16", 4096, 32768, 1, 64, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 6)
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w, M, sub=M)
+    z = cpu(m.forward(torch.from_numpy(h).cuda()))
+    _check(z, of.forward(model, h), TOL_BF16, f"wide down M={M}")
+
+
+@gpu
 @pytest.mark.parametrize("kind", ["skinny", "tiled"])
 @pytest.mark.parametrize("M", [17, 40, 64, 100, 128, 160])
 def test_bf16_forward_kernel_families(M, kind, monkeypatch):

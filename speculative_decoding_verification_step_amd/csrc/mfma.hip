@@ -272,20 +272,17 @@ hipError_t launch_mf(const MatmulArgs& a, const uint16_t* act, void* out, int Mc
                      size_t stride, hipStream_t stream) {
     if (a.act_tiled) {
         // activations in the operand layout (9..128 rows per pass): each
-        // activation load is one contiguous KiB.  The LM head runs eight
-        // fragments per wave at 17..64 rows (two row groups x two k slices on
-        // a vocabulary of 400+ 256-row groups); the rest four fragments per
-        // wave and eight k slices (two-step buffers up to 64 rows, one above).
+        // activation load is one contiguous KiB.  Four fragments per wave and
+        // eight k slices (two-step buffers up to 64 rows, one above); eight
+        // fragments per wave for the LM head at 17..64 rows and for wide
+        // projections at 17..48 (skinny_wide).
         if (!a.tiled) return hipErrorInvalidValue;
         if constexpr (EPI != kEpiStore && MF >= 2 && MF <= 3) {
             if (skinny_wide(a.M, a.N, a.K, EPI))
                 return launch_shape<MF, 8, 1, 8, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
         }
-        if constexpr (EPI == kEpiStore && MF >= 2 && MF <= 4) {
-            if ((a.N + 255) / 256 >= 400)
-                return launch_shape<MF, 8, 2, 2, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
-            return launch_shape<MF, 8, 1, 4, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
-        }
+        if constexpr (EPI == kEpiStore && MF >= 2 && MF <= 4)
+            return launch_shape<MF, 8, 1, 8, 1, EPI, true>(a, act, out, Mc, ksg, stride, stream);
         return launch_shape<MF, 4, 1, 8, (MF <= 4 ? 2 : 1), EPI, true>(a, act, out, Mc, ksg, stride,
                                                                         stream);
     }

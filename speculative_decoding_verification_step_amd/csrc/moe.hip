@@ -311,6 +311,89 @@ __global__ __launch_bounds__(kRouteThreads) void moe_sort_kernel(
     sort_pairs<kRouteThreads>(lsel, M, E, k, pad, cnt, loff, offs, perm, inv, alist, nact, active);
 }
 
+// Routing of up to 6 positions in one workgroup: router scores, top_k and
+// the sort without two launches in between.  Wave w takes expert fragment w
+// / wpf (wpf = 16 / fragments waves per fragment) and the w % wpf-th slice of
+// its reduction steps, with the positions as the B operand (rows past M read
+// as zeros); the slices are summed in slice order, then top_k (one wave per
+// position, selections kept in LDS) and the counting sort run as in the
+// separate kernels.  One CU reads all the router weights, so the separate
+// kernels (router spread over the chip) catch up at about 8 positions
+// (64-expert workload, forward: -5% at 1 position, -1% at 5, +0.5% at 8,
+// +3% at 16).
+constexpr int kRouteSmallRows = 6;
+constexpr int kRouteBatch = 8;
+constexpr int kRouteSmallMaxSteps = 32;   // steps per wave: more take the separate kernels
+
+// Whether the routing of M positions runs in one workgroup (each wave's
+// slice at most kRouteSmallMaxSteps steps).
+bool route_small(int M, int E, int d) {
+    const int nfe = (E + 15) / 16;
+    const int wpf = (kRouteThreads / kWave) / nfe;
+    return M <= kRouteSmallRows && (d / 32 + wpf - 1) / wpf <= kRouteSmallMaxSteps;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_small_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ Wr, int M, int E, int Ep, int d,
+    int k, int pad, float* __restrict__ wts, int32_t* __restrict__ offs,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ alist,
+    int32_t* __restrict__ nact, int32_t* __restrict__ active) {
+    constexpr int NW = kRouteThreads / kWave;
+    __shared__ float zs[kRouteSmallRows * kMoeMaxExperts];
+    __shared__ f32x4v part[NW][kWave];
+    __shared__ int32_t lsel[kRouteSmallRows * kMoeMaxTopK];
+    __shared__ int32_t cnt[kMoeMaxExperts];
+    __shared__ int32_t loff[kMoeMaxExperts + 1];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int S = d / 32;
+    const int nfe = (E + 15) / 16;                 // <= 16 (E <= 256)
+    const int wpf = NW / nfe;
+    const int fe = wave / wpf, ks = wave % wpf;    // fe >= nfe: idle wave
+    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+    if (fe < nfe) {
+        const int r16 = lane & 15, g = lane >> 4;
+        const int s0 = S * ks / wpf, s1 = S * (ks + 1) / wpf;
+        const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        // kRouteBatch steps of loads in flight before their products (steps
+        // past the slice read as zeros)
+        for (int s = s0; s < s1; s += kRouteBatch) {
+            bf16x8 w[kRouteBatch], x[kRouteBatch];
+#pragma unroll
+            for (int u = 0; u < kRouteBatch; ++u) {
+                const bool in = s + u < s1;
+                w[u] = in ? *reinterpret_cast<const bf16x8*>(Wr + ((size_t)fe * S + s + u) * 512 + lane * 8)
+                          : zero8;
+                x[u] = in && r16 < M
+                           ? *reinterpret_cast<const bf16x8*>(a + (size_t)r16 * d + 32 * (s + u) + 8 * g)
+                           : zero8;
+            }
+#pragma unroll
+            for (int u = 0; u < kRouteBatch; ++u)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[u], x[u], acc, 0, 0, 0);
+        }
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    // lane 16 (e % 16 / 4) + t, element e % 4 of fragment e / 16 holds
+    // expert e of position t; a NaN score and the padding columns are -inf
+    for (int i = threadIdx.x; i < kRouteSmallRows * Ep; i += kRouteThreads) {
+        const int t = i / Ep, e = i - t * Ep;
+        float z = -INFINITY;
+        if (t < M && e < E) {
+            const int f = e / 16, ii = e & 15;
+            const int l = ((ii >> 2) << 4) + t;
+            float v = 0.f;
+            for (int w = 0; w < wpf; ++w) v += part[f * wpf + w][l][ii & 3];
+            z = v == v ? v : -INFINITY;
+        }
+        zs[i] = z;
+    }
+    __syncthreads();
+    topk_rows<kRouteThreads>(zs, M, E, Ep, k, 0, lsel, wts);
+    __syncthreads();
+    sort_pairs<kRouteThreads>(lsel, M, E, k, pad, cnt, loff, offs, perm, inv, alist, nact, active);
+}
+
 // ---- grouped matmul -------------------------------------------------------------
 // out[row, n] = sum_c act[src(row), c] * W_e[n, c] for the rows row of expert
 // e (offs[e] .. offs[e+1]); src(row) = perm[row] / top_k (gather of the
@@ -627,29 +710,39 @@ int spec_verify_moe_forward(const sv_moe* model, const float* hidden, int32_t M,
         const uint16_t* wr = static_cast<const uint16_t*>(d.w_router) + (size_t)l * router_stride;
         int32_t* act_out = active_experts ? active_experts + l : nullptr;
         const int Ep = (E + 3) & ~3;
-        {
-            ProfScope prof("moe_router", s, (double)E * d.d * 2 + (double)M * d.d * 2,
+        if (route_small(M, E, d.d)) {
+            ProfScope prof("moe_route", s, (double)E * d.d * 2 + (double)M * d.d * 2,
                            2.0 * M * E * (double)d.d);
-            const dim3 grid((unsigned)((E + 15) / 16), (unsigned)p.router_splits,
-                            (unsigned)((M + 63) / 64));
-            SV_LAUNCH(prof, moe_router_kernel, grid, kRouterWaves * kWave, s,
-                      static_cast<const uint16_t*>(a), wr, M, E, d.d, p.router_spw, part);
+            SV_LAUNCH(prof, moe_route_small_kernel, 1, kRouteThreads, s,
+                      static_cast<const uint16_t*>(a), wr, M, E, Ep, d.d, k, p.act_tiled, wts,
+                      offs, perm, inv, alist, nact, act_out);
             e = hipGetLastError();
-            if (e != hipSuccess) return moe_hip_fail(e, "router launch");
-        }
-        {
-            ProfScope prof("moe_topk", s, (double)p.router_splits * M * E * 4, 0.0);
-            SV_LAUNCH(prof, moe_topk_kernel, (unsigned)((M + 3) / 4), 256, s, part,
-                      p.router_splits, M, E, Ep, k, sel, wts);
-            e = hipGetLastError();
-            if (e != hipSuccess) return moe_hip_fail(e, "top-k launch");
-        }
-        {
-            ProfScope prof("moe_sort", s, (double)M * k * 12, 0.0);
-            SV_LAUNCH(prof, moe_sort_kernel, 1, kRouteThreads, s, sel, M, E, k, p.act_tiled, offs,
-                      perm, inv, alist, nact, act_out);
-            e = hipGetLastError();
-            if (e != hipSuccess) return moe_hip_fail(e, "sort launch");
+            if (e != hipSuccess) return moe_hip_fail(e, "routing launch");
+        } else {
+            {
+                ProfScope prof("moe_router", s, (double)E * d.d * 2 + (double)M * d.d * 2,
+                               2.0 * M * E * (double)d.d);
+                const dim3 grid((unsigned)((E + 15) / 16), (unsigned)p.router_splits,
+                                (unsigned)((M + 63) / 64));
+                SV_LAUNCH(prof, moe_router_kernel, grid, kRouterWaves * kWave, s,
+                          static_cast<const uint16_t*>(a), wr, M, E, d.d, p.router_spw, part);
+                e = hipGetLastError();
+                if (e != hipSuccess) return moe_hip_fail(e, "router launch");
+            }
+            {
+                ProfScope prof("moe_topk", s, (double)p.router_splits * M * E * 4, 0.0);
+                SV_LAUNCH(prof, moe_topk_kernel, (unsigned)((M + 3) / 4), 256, s, part,
+                          p.router_splits, M, E, Ep, k, sel, wts);
+                e = hipGetLastError();
+                if (e != hipSuccess) return moe_hip_fail(e, "top-k launch");
+            }
+            {
+                ProfScope prof("moe_sort", s, (double)M * k * 12, 0.0);
+                SV_LAUNCH(prof, moe_sort_kernel, 1, kRouteThreads, s, sel, M, E, k, p.act_tiled, offs,
+                          perm, inv, alist, nact, act_out);
+                e = hipGetLastError();
+                if (e != hipSuccess) return moe_hip_fail(e, "sort launch");
+            }
         }
         const int listed = E < M * k ? E : M * k;   // experts a block can use
         {

@@ -88,13 +88,14 @@ def test_moe_forward_is_deterministic():
 
 
 @gpu
-@pytest.mark.parametrize("M", [7, 100])
+@pytest.mark.parametrize("M", [4, 7, 100])
 def test_exact_router_ties(M):
     """Every expert of a block has the same router row, so all scores tie
     exactly (in fp64 and in the kernel's fp32 alike): ties go to the lower
     id, so experts 0 .. k-1 serve every position with equal weights.  No row
-    is set aside here: the rule decides, not the summation order.  M = 7
-    leaves a ragged top-k workgroup; M = 100 spans two router row blocks."""
+    is set aside here: the rule decides, not the summation order.  M = 4
+    routes in one workgroup; M = 7 leaves a ragged top-k workgroup; M = 100
+    spans two router row blocks."""
     sv = require_gpu()
     for E, k in ((2, 1), (8, 3)):
         w = workload.MoEWorkload("moe-ties", 128, 64, E, k, 2, 333, 1, 4, 0.3, 1.0, 11)

@@ -15,11 +15,13 @@
 // partial planes that the next RMSNorm folds in, in split order.
 //
 // Every weight fragment needs one 1 KiB load and every activation fragment
-// another, so the activation loads per weight byte fall as MF / RF: one
-// fragment per wave suits up to 8 rows, two suit 9..16 rows of a wide
-// projection, four or eight 9..128 rows.  Up to 8 rows the activations are
-// row-major (rows past M cost nothing); from 9 rows they come in the operand
-// layout, where each activation load is one contiguous KiB.
+// another, so a wave loads MF / RF activation bytes per weight byte.  One
+// fragment per wave suits up to 8 rows; from 9 rows four fragments per wave
+// share each activation load, and eight where the grid still fills the chip
+// (the LM head at 17..64 rows, wide projections at 17..48: skinny_wide).  Up
+// to 8 rows the activations are row-major (rows past M cost nothing); from 9
+// rows they come in the operand layout, where each activation load is one
+// contiguous KiB.
 //
 // Weights come either row-major or packed in the tiled layout of pack.hip,
 // where each 16 x 32 operand block is one contiguous KiB in lane order (one

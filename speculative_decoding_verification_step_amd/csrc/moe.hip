@@ -420,8 +420,13 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void moe_grouped_kernel(
     const int nfr = (nfrag + RF - 1) / RF;
     const int li = blockIdx.x / nfr;
     const int f0 = (blockIdx.x % nfr) * RF;
-    if (li >= *nact) return;               // fewer experts in use than the launch allows
+    // the count of experts in use and this workgroup's entry are read
+    // together (li < listed <= E, and alist holds E entries), so the weight
+    // address waits for one memory round trip, not two
+    const int used = *nact;
     const int e = alist[li];
+    asm volatile("" ::"s"(used), "s"(e));  // both loads before the branch
+    if (li >= used) return;                // fewer experts in use than the launch allows
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;

@@ -45,18 +45,15 @@ constexpr float kLazyMargin = 8.0f;   // log2 units a score may exceed the runni
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// Query tiles (16 rows each) per wave: every K/V block a wave loads serves QT
-// tiles.  Two at head_dim 128 and four at 64 keep a wave's registers within
-// its share (two K/V register sets of 64 / 32 VGPRs plus QT accumulators).
-int tiles_per_wave(int nq, int Dh) {
-    if (nq <= 1) return 1;
-    if (nq == 2) return 2;
-    return Dh == 128 ? 2 : 4;
-}
+// From kRingMinTiles query tiles (16 rows each) per KV head the LDS-ring
+// kernel runs: four waves of QTW tiles share one pass of every block (QTW 1
+// or 2 at head_dim 128, up to 4 at 64; with 2 or 3 tiles some waves only help
+// copy).  A single tile runs the register kernel, one tile per wave with the
+// next block in flight.  The ring at 2 tiles measured 4-12% faster than two
+// tiles per wave in registers (8B heads, K = 7: 53.5 -> 49.5 us at B = 8,
+// 43.5 -> 38.3 us at B = 1 over 32K).
+constexpr int kRingMinTiles = 2;
 
-// From 4 query tiles per KV head the LDS-ring kernel runs instead: four waves
-// of QTW tiles share one pass of every block (QTW 1 or 2 at head_dim 128, up
-// to 4 at 64).
 int ring_tiles_per_wave(int nq, int Dh) {
     const int want = (nq + kWavesPerGroup - 1) / kWavesPerGroup;
     if (want <= 1) return 1;
@@ -76,8 +73,8 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int Dh, int max_blocks) {
     AttnPlan p;
     p.G = Hq / Hkv;
     p.nq = (p.G * T + 15) / 16;
-    p.ring = p.nq >= kWavesPerGroup;
-    p.qt = p.ring ? ring_tiles_per_wave(p.nq, Dh) : tiles_per_wave(p.nq, Dh);
+    p.ring = p.nq >= kRingMinTiles;
+    p.qt = p.ring ? ring_tiles_per_wave(p.nq, Dh) : 1;
     const int group = p.ring ? kWavesPerGroup * p.qt : p.qt;    // tiles per workgroup
     p.nqg = (p.nq + group - 1) / group;
     const long long base = (long long)B * Hkv * p.nqg;
@@ -701,13 +698,9 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
         ProfScope prof("attention", stream, kv_bytes + (double)B * T * Hq * head_dim * 6, flops);
 #define SV_ATTN(DH, DIRECT, QT)                                                             \
         SV_LAUNCH(prof, (attn_kernel<DH, DIRECT, QT>), grid, kWavesPerGroup * kWave, stream, a)
-        // tiles per wave: 1 or 2 at head_dim 128, 1, 2 or 4 at 64 (tiles_per_wave)
-#define SV_ATTN_128(DIRECT)                                                                 \
-        if (p.qt == 1) SV_ATTN(128, DIRECT, 1); else SV_ATTN(128, DIRECT, 2);
-#define SV_ATTN_64(DIRECT)                                                                  \
-        if (p.qt == 1) SV_ATTN(64, DIRECT, 1);                                              \
-        else if (p.qt == 2) SV_ATTN(64, DIRECT, 2);                                         \
-        else SV_ATTN(64, DIRECT, 4);
+        // one tile per wave (a single tile per KV head)
+#define SV_ATTN_128(DIRECT) SV_ATTN(128, DIRECT, 1);
+#define SV_ATTN_64(DIRECT) SV_ATTN(64, DIRECT, 1);
 #define SV_RING(DH, DIRECT, QTW)                                                            \
         SV_LAUNCH(prof, (attn_ring_kernel<DH, DIRECT, QTW>), grid, kWavesPerGroup * kWave, stream, a)
 #define SV_RING_128(DIRECT)                                                                 \

@@ -5,9 +5,9 @@
 // The target scores every drafted slot in one pass (NVIDIA co-design post,
 // "What is speculative decoding?"; its "Draft length and attention
 // performance": with G query heads per KV head the attention GEMM-M is
-// G (1 + D)).  One wave owns 16 of the G*T query rows of one (request, KV
-// head) and one range of KV blocks; both products run on the matrix cores
-// with the keys as the row dimension:
+// G (1 + D)).  A wave owns tiles of 16 of the G*T query rows of one
+// (request, KV head) and one range of KV blocks; both products run on the
+// matrix cores with the keys as the row dimension:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims of a block
 //                 (contiguous in k_cache), B = Q^T (each lane's query row);
 //   O^T += V^T P^T  A = V^T (16 dims x 32 keys; V is stored transposed per
@@ -18,11 +18,10 @@
 // 0, then keys 16+4g..16+4g+3 of tile 1) - the A operand V^T uses the same
 // order - so the softmax needs no transpose and no LDS; each query row's
 // running max and sum are shared by its four lane groups through two
-// shuffles.  The four waves of a workgroup take interleaved blocks of one
-// context range (each prefetching its next block into a second register
-// set) and merge their (max, sum, output) states through LDS; long contexts
-// are further split over workgroups (flash-decoding style) and the partial
-// states are merged in a second kernel in split order.  Probabilities enter
+// shuffles.  The four waves of a workgroup walk the same blocks of one
+// context range, which pass once through an LDS ring (attn_ring_kernel);
+// long contexts are further split over workgroups (flash-decoding style) and
+// the partial states are merged in a second kernel in split order.  Probabilities enter
 // the second product rounded to bf16 and the softmax sum is taken over the
 // same rounded values, so every output row is a convex combination of the
 // visible value rows.
@@ -40,20 +39,18 @@ namespace {
 constexpr int kBlk = SV_KV_BLOCK;
 constexpr int kWavesPerGroup = 4;
 constexpr int kTargetUnits = 512;     // workgroups the context split aims for (2 per CU)
-constexpr int kMinBlocksPerSplit = 8; // two blocks per wave at least
+constexpr int kMinBlocksPerSplit = 8; // KV blocks per context split at least
 constexpr float kLazyMargin = 8.0f;   // log2 units a score may exceed the running max by
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// From kRingMinTiles query tiles (16 rows each) per KV head the LDS-ring
-// kernel runs: four waves of QTW tiles share one pass of every block (QTW 1
-// or 2 at head_dim 128, up to 4 at 64; with 2 or 3 tiles some waves only help
-// copy).  A single tile runs the register kernel, one tile per wave with the
-// next block in flight.  The ring at 2 tiles measured 4-12% faster than two
-// tiles per wave in registers (8B heads, K = 7: 53.5 -> 49.5 us at B = 8,
-// 43.5 -> 38.3 us at B = 1 over 32K).
-constexpr int kRingMinTiles = 2;
-
+// Query tiles (16 rows each) per wave: four waves of QTW tiles share one
+// pass of every block (QTW 1 or 2 at head_dim 128, up to 4 at 64; with fewer
+// tiles than waves the spare waves only help copy).  Measured against a
+// kernel in which every wave streamed its own blocks into registers (next
+// block in flight), the ring was 0-8% faster with one tile per KV head and
+// 4-12% faster with two (8B heads, B = 1 over 32K: 37.1 -> 34.3 us at K = 0,
+// 43.5 -> 38.3 us at K = 7).
 int ring_tiles_per_wave(int nq, int Dh) {
     const int want = (nq + kWavesPerGroup - 1) / kWavesPerGroup;
     if (want <= 1) return 1;
@@ -63,7 +60,6 @@ int ring_tiles_per_wave(int nq, int Dh) {
 
 struct AttnPlan {
     int G = 0, nq = 0, qt = 1, nqg = 0, nsplit = 1, bps = 0;
-    int ring = 0;            // the LDS-ring kernel (qt tiles per wave, 4 waves per group)
     long long units = 0;     // workgroups: (request, KV head, split, group of qt tiles)
     long long rows16 = 0;    // 16-row partial-state slots: (request, KV head, split, tile)
     size_t ws_bytes = 0;
@@ -73,9 +69,8 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int Dh, int max_blocks) {
     AttnPlan p;
     p.G = Hq / Hkv;
     p.nq = (p.G * T + 15) / 16;
-    p.ring = p.nq >= kRingMinTiles;
-    p.qt = p.ring ? ring_tiles_per_wave(p.nq, Dh) : 1;
-    const int group = p.ring ? kWavesPerGroup * p.qt : p.qt;    // tiles per workgroup
+    p.qt = ring_tiles_per_wave(p.nq, Dh);
+    const int group = kWavesPerGroup * p.qt;    // tiles per workgroup
     p.nqg = (p.nq + group - 1) / group;
     const long long base = (long long)B * Hkv * p.nqg;
     long long ns = (kTargetUnits + base - 1) / base;
@@ -116,223 +111,8 @@ __device__ __forceinline__ int table_entry(const int32_t* row, int kb) {
     return ((const const_i32*)row)[__builtin_amdgcn_readfirstlane(kb)];
 }
 
-template <int DH>
-struct KVRegs {
-    bf16x8 k0[DH / 32], k1[DH / 32], v[DH / 16];
-};
-
-template <int DH, bool kDirect, int QT>
-__global__ __launch_bounds__(kWavesPerGroup * kWave, QT == 1 ? 2 : 1) void attn_kernel(AttnArgs a) {
-    constexpr int KS = DH / 32;   // k steps of the score product
-    constexpr int DT = DH / 16;   // 16-dim tiles of the output
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    // XCD-contiguous renumbering (workgroup i runs on XCD i % 8): the query
-    // tile groups of one (request, KV head, range) get consecutive numbers on
-    // one XCD and read its blocks through one L2
-    const int wg = blockIdx.x, Gn = gridDim.x;
-    const int q8 = Gn / 8, r8 = Gn % 8, x8 = wg % 8, j8 = wg / 8;
-    const long long unit = x8 < r8 ? x8 * (q8 + 1) + j8 : r8 * (q8 + 1) + (x8 - r8) * q8 + j8;
-    const int qg = (int)(unit % a.nqg);
-    long long rest = unit / a.nqg;
-    const int sp = (int)(rest % a.nsplit);
-    rest /= a.nsplit;
-    const int kvh = (int)(rest % a.Hkv);
-    const int b = (int)(rest / a.Hkv);
-    const int G = a.Hq / a.Hkv;
-    const int c = lane & 15, g = lane >> 4;
-    const int cap = a.max_blocks * kBlk;
-    const int ctx = clamp_ctx(a.ctx[b], cap);
-    const int n_all = min(ctx + a.T, cap);                    // positions any row may see
-    const int kb_end = min((n_all + kBlk - 1) / kBlk, (sp + 1) * a.bps);
-
-    // this lane's query row in each of the group's tiles: position t, head h
-    // (a column of S^T); tiles past the last one hold no rows
-    int t[QT], h[QT], vis[QT];
-    bool row_ok[QT], tile_ok[QT];
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-        const int qt = qg * QT + i;
-        const int r = qt * 16 + c;
-        tile_ok[i] = qt < a.nq;
-        row_ok[i] = r < G * a.T;
-        t[i] = row_ok[i] ? r / G : 0;
-        h[i] = kvh * G + r % G;
-        vis[i] = row_ok[i] ? min(ctx + t[i] + 1, cap) : 0;    // visible positions of the row
-    }
-
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    bf16x8 qv[QT][KS];
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-        const uint16_t* qrow = a.q + (((size_t)b * a.T + t[i]) * a.Hq + (h[i] < a.Hq ? h[i] : 0)) * DH;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qv[i][s] = row_ok[i] ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : zero8;
-    }
-
-    float m[QT], lpart[QT];
-    f32x4v acc[QT][DT];
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-        m[i] = -INFINITY;
-        lpart[i] = 0.f;
-#pragma unroll
-        for (int u = 0; u < DT; ++u) acc[i][u] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
-    auto load = [&](KVRegs<DH>& kv, int kb) {
-        int blk = table_entry(trow, kb);
-        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-        const uint16_t* kbase = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlk * DH;
-        const uint16_t* vbase = a.vc + ((size_t)blk * a.Hkv + kvh) * DH * kBlk;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            kv.k0[s] = *reinterpret_cast<const bf16x8*>(kbase + c * DH + 32 * s + 8 * g);
-            kv.k1[s] = *reinterpret_cast<const bf16x8*>(kbase + (16 + c) * DH + 32 * s + 8 * g);
-        }
-#pragma unroll
-        for (int u = 0; u < DT; ++u) {
-            const uint16_t* vrow = vbase + (16 * u + c) * kBlk;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-            kv.v[u] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        }
-    };
-    auto process = [&](const KVRegs<DH>& kv, int kb) {
-#pragma unroll
-        for (int i = 0; i < QT; ++i) {
-            if (!tile_ok[i]) continue;                       // uniform over the workgroup
-            f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k0[s], qv[i][s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.k1[s], qv[i][s], s1, 0, 0, 0);
-            }
-            // lane holds S^T[key 4g+j][row] in s0[j] and S^T[key 16+4g+j][row] in s1[j]
-            const int p0 = kb * kBlk + 4 * g;
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[j] = p0 + j < vis[i] ? s0[j] * a.scale_log2 : -INFINITY;
-                x[4 + j] = p0 + 16 + j < vis[i] ? s1[j] * a.scale_log2 : -INFINITY;
-            }
-            // Lazy running max: the reference m (equal in the row's four lane
-            // groups) moves only when some score exceeds it by more than
-            // kLazyMargin (log2 units), found with one wave-wide vote; the
-            // exact row max and the rescale then run.  Otherwise p <= 2^margin
-            // and no cross-lane exchange is needed; the sum stays per lane group.
-            float lm = x[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) lm = fmaxf(lm, x[j]);
-            if (__ballot(lm > m[i] + kLazyMargin)) {
-                float bm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
-                bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-                const float mn = fmaxf(m[i], bm);
-                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
-                lpart[i] *= alpha;
-#pragma unroll
-                for (int u = 0; u < DT; ++u) acc[i][u] *= alpha;
-                m[i] = mn;
-            }
-            const float mref = m[i] == -INFINITY ? 0.f : m[i];   // no visible key yet: p = 0
-            uint32_t pw[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pw[j] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * j] - mref),
-                                    __builtin_amdgcn_exp2f(x[2 * j + 1] - mref));
-                lpart[i] += bf16lo(pw[j]);     // in key order, as the product sums them
-                lpart[i] += bf16hi(pw[j]);
-            }
-            const bf16x8 pv = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-#pragma unroll
-            for (int u = 0; u < DT; ++u)
-                acc[i][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv.v[u], pv, acc[i][u], 0, 0, 0);
-        }
-    };
-
-    // this wave's blocks: kb0 + wave, + 4, + 8, ..., the next one always in
-    // flight.  The wave index is made provably uniform, so block ids come
-    // through scalar loads, and the loop body has no branch around its loads:
-    // the wait before a block's products then covers only the older block.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int first = sp * a.bps + wv;
-    const int nmine = first < kb_end ? (kb_end - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-    const int last = first + kWavesPerGroup * (nmine - 1);
-    KVRegs<DH> bufa, bufb;
-    if (nmine > 0) {
-        int kb = first;
-        load(bufa, kb);
-        for (int i = 0;; i += 2) {
-            load(bufb, min(kb + kWavesPerGroup, last));
-            process(bufa, kb);
-            if (i + 1 >= nmine) break;
-            load(bufa, min(kb + 2 * kWavesPerGroup, last));
-            process(bufb, kb + kWavesPerGroup);
-            if (i + 2 >= nmine) break;
-            kb += 2 * kWavesPerGroup;
-        }
-    }
-
-    // merge the four waves' states (fixed wave order), one tile at a time;
-    // lane holds O^T[dim 16u+4g+j][row] in acc[i][u][j], and (m, l) of its row
-    __shared__ float sm[kWavesPerGroup][16], sl[kWavesPerGroup][16];
-    __shared__ f32x4v so[kWavesPerGroup][DT][kWave];
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-        if (!tile_ok[i]) continue;                           // uniform over the workgroup
-        // the row's softmax sum over its four lane groups
-        float l = lpart[i] + __shfl_xor(lpart[i], 16, kWave);
-        l += __shfl_xor(l, 32, kWave);
-        if (i) __syncthreads();                              // the previous tile's readers are done
-        if (g == 0) {
-            sm[wave][c] = m[i];
-            sl[wave][c] = l;
-        }
-#pragma unroll
-        for (int u = 0; u < DT; ++u) so[wave][u][lane] = acc[i][u];
-        __syncthreads();
-        float M = sm[0][c];
-#pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) M = fmaxf(M, sm[w][c]);
-        float e[kWavesPerGroup], L = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w) {
-            e[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][c] - M);
-            L += e[w] * sl[w][c];
-        }
-        // the partial-state slot of this tile: (request, KV head, split, tile)
-        const long long slot = (((long long)b * a.Hkv + kvh) * a.nsplit + sp) * a.nq + qg * QT + i;
-        const size_t prow = (size_t)slot * 16 + c;
-        // wave w finishes the output tiles u = w, w + 4, ...
-#pragma unroll
-        for (int u = wave; u < DT; u += kWavesPerGroup) {
-            f32x4v o = e[0] * so[0][u][lane];
-#pragma unroll
-            for (int w = 1; w < kWavesPerGroup; ++w) o += e[w] * so[w][u][lane];
-            if constexpr (kDirect) {
-                if (row_ok[i]) {
-                    const float inv = L > 0.f ? 1.0f / L : 0.f;
-                    *reinterpret_cast<f32x4v*>(a.out + (((size_t)b * a.T + t[i]) * a.Hq + h[i]) * DH +
-                                               16 * u + 4 * g) = o * inv;
-                }
-            } else {
-                *reinterpret_cast<f32x4v*>(a.part_o + prow * DH + 16 * u + 4 * g) = o;
-            }
-        }
-        if constexpr (!kDirect) {
-            if (wave == 0 && g == 0) {
-                a.part_ml[2 * prow] = M;
-                a.part_ml[2 * prow + 1] = L;
-            }
-        }
-    }
-}
-
-
-// From 4 query tiles per KV head: the four waves own QTW tiles each (4 * QTW
-// tiles = up to 128 query rows per workgroup) and walk the SAME blocks of the
+// The four waves own QTW tiles each (4 * QTW tiles = up to 128 query rows per
+// workgroup; tiles past the last one are skipped) and walk the SAME blocks of the
 // context range, which pass once through a ring of kRingStages LDS stages
 // (global_load_lds_dwordx4) two blocks at a time: the next pair's copies are
 // in flight while a pair is used, paced by vmcnt and one bare barrier per pair
@@ -482,6 +262,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, QTW <= 2 ? 2 : 1) void attn
             float lm = x[0];
 #pragma unroll
             for (int j = 1; j < 8; ++j) lm = fmaxf(lm, x[j]);
+            // Lazy running max: the reference m (equal in the row's four lane
+            // groups) moves only when some score exceeds it by more than
+            // kLazyMargin (log2 units), found with one wave-wide vote; the
+            // exact row max and the rescale then run.  Otherwise p <= 2^margin
+            // and no cross-lane exchange is needed; the sum stays per lane group.
             if (__ballot(lm > m[q] + kLazyMargin)) {
                 float bm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
                 bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
@@ -696,11 +481,6 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
     const double flops = 4.0 * B * Hq * T * (double)max_blocks * kBlk * head_dim;
     {
         ProfScope prof("attention", stream, kv_bytes + (double)B * T * Hq * head_dim * 6, flops);
-#define SV_ATTN(DH, DIRECT, QT)                                                             \
-        SV_LAUNCH(prof, (attn_kernel<DH, DIRECT, QT>), grid, kWavesPerGroup * kWave, stream, a)
-        // one tile per wave (a single tile per KV head)
-#define SV_ATTN_128(DIRECT) SV_ATTN(128, DIRECT, 1);
-#define SV_ATTN_64(DIRECT) SV_ATTN(64, DIRECT, 1);
 #define SV_RING(DH, DIRECT, QTW)                                                            \
         SV_LAUNCH(prof, (attn_ring_kernel<DH, DIRECT, QTW>), grid, kWavesPerGroup * kWave, stream, a)
 #define SV_RING_128(DIRECT)                                                                 \
@@ -709,23 +489,14 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
         if (p.qt == 1) SV_RING(64, DIRECT, 1);                                              \
         else if (p.qt == 2) SV_RING(64, DIRECT, 2);                                         \
         else SV_RING(64, DIRECT, 4);
-        if (p.ring) {
-            if (head_dim == 128) {
-                if (p.nsplit > 1) { SV_RING_128(false) } else { SV_RING_128(true) }
-            } else {
-                if (p.nsplit > 1) { SV_RING_64(false) } else { SV_RING_64(true) }
-            }
-        } else if (head_dim == 128) {
-            if (p.nsplit > 1) { SV_ATTN_128(false) } else { SV_ATTN_128(true) }
+        if (head_dim == 128) {
+            if (p.nsplit > 1) { SV_RING_128(false) } else { SV_RING_128(true) }
         } else {
-            if (p.nsplit > 1) { SV_ATTN_64(false) } else { SV_ATTN_64(true) }
+            if (p.nsplit > 1) { SV_RING_64(false) } else { SV_RING_64(true) }
         }
 #undef SV_RING_64
 #undef SV_RING_128
 #undef SV_RING
-#undef SV_ATTN_64
-#undef SV_ATTN_128
-#undef SV_ATTN
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return launch_fail(e, "attention launch");

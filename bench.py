@@ -8,11 +8,14 @@ resident in HBM before timing starts.  The steps are launched eagerly,
 back to back on one stream (measured faster than HIP graph replay on this
 stack: about 1 us per graph node); the graph-replay time is reported too.
 
-Prints ONE JSON line.  Default workload: the 8B-shaped stack at B=1, K=4
-(d=4096, ffn=14336, L=8, V=32000, bf16, sigma=0.3, T=1).
+Prints ONE JSON line.  Default (headline) workload: the large-batch step,
+B=256, K=2 (d=4096, ffn=14336, L=8, V=128256, bf16, sigma=0.5, T=0.7), the
+largest single-GPU configuration; the same line carries nested records
+("workloads") of the 70B-layer share (B=8, K=4) and the 8B-shaped step
+(B=1, K=4), each with its own roofline.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
-                    [--no-cpu-baseline] [--sweep]
+                    [--no-cpu-baseline] [--no-nested] [--sweep]
 
 ``--sweep`` instead prints one JSON line per (B, K, sigma) point of the
 8B-shaped stack (B in 1,4,16,64; K in 1,2,4,8).  ``--crossover`` prints the
@@ -44,6 +47,14 @@ METRIC = "verified positions/sec + accepted tokens/sec vs B,K; % HBM / % MFMA ro
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16
 VALU_F32_PEAK_TFS = 157.3
+# the headline: the largest single-GPU configuration (B=256, K=2, M=768); the
+# line also carries these workloads as nested records
+HEADLINE = "large-batch-b256-k2"
+NESTED = ("70b-layer-share-b8-k4", "8b-shaped-b1-k4")
+NESTED_KEYS = ("config", "ms_per_step", "accepted_tokens_per_s", "mean_accept_len",
+               "accept_len_hist", "step_ms_p10_p50_p90", "step_hbm_frac", "step_mfma_frac",
+               "roofline_step_ms", "forward_ms", "forward_hbm_frac", "forward_mfma_frac",
+               "accept_ms", "graph_ms_per_step", "eager_ms_per_step", "roofline", "kernels")
 # row counts B*(K+1) of the crossover scan (the sweep's B x K grid spans 2..576)
 CROSSOVER_ROWS = (16, 32, 48, 64, 80, 96, 128, 144, 192, 256, 320, 384, 512, 576, 768)
 
@@ -280,34 +291,67 @@ def _profile_kernels(sv, one, s, reps):
     return sv.profile_end(64)
 
 
-def _cpu_baseline(host, w, B, K, T, seed, budget_s=20.0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    from oracle import forward as of, verify as ov
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    nreq = 1
-    rows = list(range(nreq * (K + 1)))
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _cpu_baseline(host, w, B, K, T, seed):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    one request (its K + 1 positions) through the fp64 forward of every block
+    and the head (the oracle upcasts each weight matrix from bf16 as it goes,
+    so every step reads all the weights, as the GPU step does) and its
+    rejection sampling.  Two legs: all the host's BLAS threads, and one
+    thread; each reports the median of 5 steps (3 on a 128256-row vocabulary
+    with 8 blocks) after one untimed step."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import forward as of, verify as ov
+    n_steps = 3 if w.weight_elems() > 1.2e9 else 5
+    rows = list(range(K + 1))
     hidden = workload.make_hidden(w, B * (K + 1))[rows]
     g = np.random.default_rng(seed)
-    zd = g.standard_normal((nreq, K, w.vocab)) * math.sqrt(w.d) * w.weight_std
+    zd = g.standard_normal((1, K, w.vocab)) * math.sqrt(w.d) * w.weight_std
     x = ov.sample_draft_tokens(zd, T, seed, 0)
-    t0 = time.perf_counter()
-    n = 0
-    while True:
+    es = 2 if w.wdtype == "bf16" else 4
+    wbytes = w.weight_elems() * es
+
+    def one(stp):
         z = of.forward(host, hidden)
-        ov.verify(z.reshape(nreq, K + 1, w.vocab), zd, x, T, seed, n)
-        n += 1
-        if time.perf_counter() - t0 > budget_s / 2 or n >= 3:
-            break
-    el = time.perf_counter() - t0
-    return {"value": n * len(rows) / el, "unit": "verified positions/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} oracle step(s) of one request ({len(rows)} positions: fp64 forward "
-                      f"through all {w.n_layers} blocks and the head, then rejection sampling), "
-                      f"{el:.1f} s"}
+        ov.verify(z.reshape(1, K + 1, w.vocab), zd, x, T, seed, stp)
+
+    def leg(threads):
+        with threadpool_limits(limits=threads):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            one(0)
+            ts = []
+            for stp in range(n_steps):
+                t0 = time.perf_counter()
+                one(stp + 1)
+                ts.append(time.perf_counter() - t0)
+        med = float(np.median(ts))
+        return {"threads": int(used), "median_step_s": med, "steps": n_steps,
+                "verified_positions_per_s": len(rows) / med,
+                "effective_weight_GBps": wbytes / med / 1e9}
+
+    print(f"[bench] cpu baseline (oracle) on {w.name}: all threads", file=sys.stderr, flush=True)
+    all_cores = leg(None)
+    print(f"[bench] cpu baseline (oracle) on {w.name}: one thread", file=sys.stderr, flush=True)
+    one_core = leg(1)
+    return {"value": all_cores["verified_positions_per_s"], "unit": "verified positions/s",
+            "cores": all_cores["threads"], "kind": "oracle",
+            "sample": f"one request of the {w.name} step ({len(rows)} positions): the oracle's fp64 "
+                      f"forward through all {w.n_layers} blocks and the head (weights upcast from "
+                      f"storage inside each step) and its rejection sampling; median of {n_steps} "
+                      f"steps after one untimed step",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "all_threads": all_cores, "one_thread": one_core}
 
 
 def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile=True):
@@ -689,7 +733,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="8b-shaped-b1-k4", choices=sorted(workload.WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(workload.WORKLOADS))
     ap.add_argument("--B", type=int)
     ap.add_argument("--K", type=int)
     ap.add_argument("--sigma", type=float)
@@ -700,6 +744,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help=argparse.SUPPRESS)  # the default
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-nested", action="store_true",
+                    help="headline workload only (no nested records of the other workloads)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--moe", action="store_true",
                     help="mixture-of-experts target: step time, experts touched and HBM roofline per "
@@ -776,8 +822,18 @@ def main():
     K = w.K if a.K is None else a.K
     sigma = w.sigma if a.sigma is None else a.sigma
     T = w.temperature if a.T is None else a.T
+    print(f"[bench] {w.name}: B={B} K={K}, {a.steps} timed steps", file=sys.stderr, flush=True)
     res = run_point(w, B, K, sigma, T, a.steps, a.warmup, a.graph, not a.no_cpu_baseline,
                     profile=not a.no_profile)
+    if w.name == HEADLINE and (a.B, a.K, a.sigma, a.T) == (None, None, None, None) and not a.no_nested:
+        res["workloads"] = {}
+        for name in NESTED:
+            wn = workload.WORKLOADS[name]
+            print(f"[bench] nested {name}: B={wn.B} K={wn.K}", file=sys.stderr, flush=True)
+            r = run_point(wn, wn.B, wn.K, wn.sigma, wn.temperature, a.steps, a.warmup, a.graph,
+                          False, profile=not a.no_profile)
+            res["workloads"][name] = {k: r[k] for k in NESTED_KEYS if k in r}
+            res["workloads"][name]["verified_positions_per_s"] = r["value"]
     print(json.dumps(res), flush=True)
     if a.calib_copy:
         # a plain copy of known size: 256 MiB read + 256 MiB written, so the

@@ -53,8 +53,9 @@ int spec_verify_choose_k(const int32_t* m_rows, const double* t_verif, int32_t n
 
 /* Speculation window from recent acceptance lengths.
  *
- * publishertech, "Speculative Decoding in Large Language Models", section 5
- * (draft-model drift mitigation, dynamic window sizing): when the running
+ * mohashari, "Speculative Decoding in Production", section "Production
+ * Failure Modes and Mitigation Strategies", item 1 "Draft Acceptance Rate
+ * Collapse (Entropy Shift)" (dynamic window sizing): when the running
  * average of accepted tokens per request over the last few requests falls
  * below a threshold (the page: 1.5 over the last 10), the window K drops
  * from its normal value (the page: 5) to a small one (1 or 2).  "Accepted

@@ -11,9 +11,12 @@ may import this package; the library never does.
 * ``speedup_vs_no_draft``: the NVIDIA co-design post's speedup
   T_verif(B) AL / (T_verif(B (1 + D)) + T_draft(B, D)) (section "What is
   speculative decoding?").
-* ``window_k``: publishertech section 5's dynamic window sizing: the reduced
-  window when the mean acceptance length over the last `window` requests is
-  below the threshold (1.5 over 10 on the page), else the normal one.
+* ``window_k``: the dynamic window sizing of mohashari "Speculative
+  Decoding in Production", section "Production Failure Modes and Mitigation
+  Strategies", item 1 "Draft Acceptance Rate Collapse (Entropy Shift)": the
+  reduced window when the mean acceptance length over the last `window`
+  requests is below the threshold (1.5 over 10 on the page), else the
+  normal one.
 
 Pinned by: the pages' printed speedups (3.52 at E[N] = 4.4, gamma = 5,
 c = 0.05; 1.13 / 0.94 at alpha = 0.3) reproduced as goodput ratios with a

@@ -16,12 +16,17 @@ rounded to bf16 (round to nearest even) when the weights are bf16, because
 the product is defined as bf16 inputs with fp32-or-better accumulation.  With
 fp32 weights nothing is rounded.
 
-``accum="f32"`` runs the same block order with fp32 matmuls (BLAS sgemm) and
-the same bf16 rounding points.  It exists only to measure how far two valid
-accumulation orders of this contract drift apart through the stack (each
-bf16 rounding decision can flip when the pre-rounding value moves by one
-fp32 rounding, and a random MLP stack amplifies the flips layer by layer);
-comparisons against the GPU use the fp64 default.
+``accum="f32"`` evaluates the same contract in fp32 wherever the contract
+allows fp32 -- matmuls (BLAS sgemm), the residual stream, the RMSNorm and the
+SiLU -- with the same bf16 rounding points.  It exists only to measure how
+far two valid evaluations of this contract drift apart through the stack
+(each bf16 rounding decision can flip when the pre-rounding value moves by
+one fp32 rounding, and a random MLP stack amplifies the flips layer by
+layer); comparisons against the GPU use the fp64 default.  ``k_order``
+(fp32 only) picks one of many equally valid summation orders: order 0 sums
+the reduction index in storage order, order n > 0 in a seeded permutation of
+it (the same permutation on both operands, so only the rounding sequence
+changes).
 
 Pinned by: torch.nn.functional (rms_norm, silu, linear) in float64 composed
 in the same block order; special cases (zero down weights leave h unchanged;
@@ -67,39 +72,62 @@ def silu(u: np.ndarray) -> np.ndarray:
 _ACCUM = {"f64": np.float64, "f32": np.float32}
 
 
-def head(a_f: np.ndarray, w_head: np.ndarray, accum: str = "f64") -> np.ndarray:
+def _perm(k_order: int, K: int, *tag) -> np.ndarray | None:
+    """The seeded reduction-index permutation of order k_order (None: storage order)."""
+    if not k_order:
+        return None
+    return np.random.default_rng((k_order, *tag)).permutation(K)
+
+
+def _mm(a: np.ndarray, w: np.ndarray, perm) -> np.ndarray:
+    """a . w^T, summing the shared index in the order perm (None: as stored)."""
+    if perm is None:
+        return a @ w.T
+    return a[:, perm] @ w[:, perm].T
+
+
+def head(a_f: np.ndarray, w_head: np.ndarray, accum: str = "f64", k_order: int = 0) -> np.ndarray:
     """Logits a_f . W_head^T, taking the head in row blocks to bound memory."""
     dt = _ACCUM[accum]
     V = w_head.shape[0]
     out = np.empty((a_f.shape[0], V), dtype=np.float64)
     a = a_f.astype(dt)
+    perm = _perm(k_order, a.shape[1], 0x4EAD)
     for lo in range(0, V, _HEAD_ROWS):
         hi = min(lo + _HEAD_ROWS, V)
-        out[:, lo:hi] = a @ weights_f64(w_head, lo, hi, dt).T
+        out[:, lo:hi] = _mm(a, weights_f64(w_head, lo, hi, dt), perm)
     return out
 
 
 def final_activation(model: dict, hidden: np.ndarray, eps: float = RMS_EPS,
-                     accum: str = "f64") -> np.ndarray:
-    """Run the L blocks and the final norm; returns a_f [rows, d] (fp64)."""
+                     accum: str = "f64", k_order: int = 0) -> np.ndarray:
+    """Run the L blocks and the final norm; returns a_f [rows, d] (fp64 values;
+    with accum="f32" every step is evaluated in fp32)."""
     dt = _ACCUM[accum]
     rnd = bf16_round if model["w_up"].dtype == np.uint16 else (lambda v: v)
-    h = np.asarray(hidden, dtype=np.float64)
-    g = np.asarray(model["gain"], dtype=np.float64)
-    L = model["w_up"].shape[0]
+
+    def rnd_dt(v):
+        return rnd(np.asarray(v, dtype=np.float64)).astype(dt)
+
+    h = np.asarray(hidden, dtype=dt)
+    g = np.asarray(model["gain"], dtype=dt)
+    L, ffn, d = model["w_up"].shape
     for l in range(L):
-        a = rnd(rmsnorm(h, g[l], eps)).astype(dt)
-        s = rnd(silu((a @ weights_f64(model["w_up"][l], dtype=dt).T).astype(np.float64))).astype(dt)
-        h = h + (s @ weights_f64(model["w_down"][l], dtype=dt).T).astype(np.float64)
-    return rnd(rmsnorm(h, g[L], eps))
+        a = rnd_dt(rmsnorm(h, g[l], dt(eps)))
+        u = _mm(a, weights_f64(model["w_up"][l], dtype=dt), _perm(k_order, d, l, 0))
+        s = rnd_dt(silu(u))
+        h = h + _mm(s, weights_f64(model["w_down"][l], dtype=dt), _perm(k_order, ffn, l, 1))
+    return rnd(np.asarray(rmsnorm(h, g[L], dt(eps)), dtype=np.float64))
 
 
 def forward(model: dict, hidden: np.ndarray, heads=("w_head",), eps: float = RMS_EPS,
-            accum: str = "f64"):
+            accum: str = "f64", k_order: int = 0):
     """Logits [rows, V] (fp64) for each requested head of ``model``.
     Returns one array, or a tuple when several heads are asked for."""
-    a_f = final_activation(model, hidden, eps, accum)
-    outs = tuple(head(a_f, model[name], accum) for name in heads)
+    if k_order and accum != "f32":
+        raise ValueError("k_order selects an fp32 summation order")
+    a_f = final_activation(model, hidden, eps, accum, k_order)
+    outs = tuple(head(a_f, model[name], accum, k_order) for name in heads)
     return outs[0] if len(outs) == 1 else outs
 
 

@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Writes tests/golden/bf16_stack_spread.json.
 
-For every full-size bf16 workload, the oracle's logits on the rows the GPU
-forward tests sample are computed twice: with fp64 accumulation (the
-reference) and with fp32 accumulation in the same block order and the same
-bf16 rounding points.  Both are valid evaluations of "bf16 inputs, fp32 or
-better accumulation"; their distance is the spread that accumulation order
-alone produces through the stack, and it bounds how closely any fp32
-implementation (the GPU's included) can be expected to match the reference
-on a full stack.  Calls only ``workload`` and ``oracle``.
+For every full-size bf16 workload, the oracle's logits on every row of the
+step (all B*(K+1) positions, the rows the GPU step test compares) are
+computed with fp64 accumulation (the reference) and in fp32 (matmuls,
+residual stream, norm and SiLU in fp32, the same bf16 rounding points) in
+four summation orders of the reduction index.  Every one is a valid
+evaluation of "bf16 inputs, fp32 accumulation"; their distance from the
+reference is the spread that rounding alone produces through the stack.  The
+maximum over a few rows is set by the single worst cascade of bf16 rounding
+flips, so it varies between orders; the envelope over the orders (largest
+max and p99.9, mean of the means) is what the GPU is held to.  Calls only
+``workload`` and ``oracle``.
 
     python tests/golden/make_stack_spread.py
 """
@@ -25,26 +28,30 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import workload  # noqa: E402
 from oracle import forward as of  # noqa: E402
 
-ROWS = {
-    "8b-shaped-b1-k4": [0, 1, 2, 3, 4],
-    "70b-layer-share-b8-k4": [0, 4, 17, 35, 39],
-    "large-batch-b256-k2": [0, 1, 2, 383, 765, 767],
-}
+ORDERS = (0, 1, 2, 3)
+NAMES = ("8b-shaped-b1-k4", "70b-layer-share-b8-k4", "large-batch-b256-k2")
 
 
 def main():
-    out = {"note": __doc__.strip().splitlines()[2:9], "workloads": {}}
-    for name, rows in ROWS.items():
+    out = {"note": __doc__.strip().splitlines()[2:14], "workloads": {}}
+    for name in NAMES:
         t0 = time.time()
         w = workload.WORKLOADS[name]
         model = workload.make_model(w, draft_head=False)
-        hidden = workload.make_hidden(w)[rows]
+        hidden = workload.make_hidden(w)
         z64 = of.forward(model, hidden)
-        z32 = of.forward(model, hidden, accum="f32")
-        d = np.abs(z32 - z64)
-        out["workloads"][name] = {"rows": rows, "max_abs": float(d.max()),
-                                  "mean_abs": float(d.mean()),
-                                  "p999_abs": float(np.quantile(d, 0.999))}
+        per = []
+        for order in ORDERS:
+            d = np.abs(of.forward(model, hidden, accum="f32", k_order=order) - z64)
+            per.append({"k_order": order, "max_abs": float(d.max()), "mean_abs": float(d.mean()),
+                        "p999_abs": float(np.quantile(d, 0.999))})
+            print(name, per[-1], flush=True)
+            del d
+        out["workloads"][name] = {"rows": "all", "n_rows": int(hidden.shape[0]),
+                                  "max_abs": max(r["max_abs"] for r in per),
+                                  "mean_abs": float(np.mean([r["mean_abs"] for r in per])),
+                                  "p999_abs": max(r["p999_abs"] for r in per),
+                                  "orders": per}
         print(name, out["workloads"][name], f"{time.time() - t0:.0f}s", flush=True)
         del model
     with open(os.path.join(HERE, "bf16_stack_spread.json"), "w") as f:

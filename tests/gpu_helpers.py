@@ -103,28 +103,47 @@ TOL_F32 = 1e-4           # logits, fp32 stack
 
 _SPREAD_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                             "bf16_stack_spread.json")
+SPREAD_MAX_FACTOR = 1.1
 
 
-def full_stack_tol(name: str) -> float:
-    """Logit tolerance for a full bf16 stack: the stated 2e-2, or 1.5x the
-    spread between two valid accumulation orders of the oracle itself on the
-    same rows (tests/golden/bf16_stack_spread.json), whichever is larger."""
+def _spread(name: str) -> dict:
     with open(_SPREAD_FILE) as f:
-        spread = json.load(f)["workloads"]
-    if name not in spread:
-        return TOL_BF16
-    return max(TOL_BF16, 1.5 * spread[name]["max_abs"])
+        return json.load(f)["workloads"][name]
 
 
-def spread_mean(name: str) -> float:
-    with open(_SPREAD_FILE) as f:
-        return json.load(f)["workloads"][name]["mean_abs"]
+def check_full_stack(err: np.ndarray, name: str, label: str):
+    """Logit error of a full bf16 stack (all rows of the step, or a sample of
+    them).  The stated 2e-2 holds for 99.9% of the logits; the maximum is held
+    to 1.1x the spread between two valid accumulation orders of the oracle
+    itself (fp64 vs fp32, same bf16 rounding points) over all rows of the
+    step (tests/golden/bf16_stack_spread.json): a random 8-block MLP stack
+    amplifies single bf16 rounding flips beyond 2e-2 at the far tail for any
+    fp32-accumulating evaluation, the oracle's own included."""
+    sp = _spread(name)
+    p999 = float(np.quantile(err, 0.999))
+    mx = float(err.max())
+    note(f"  {label}: max |dlogit| = {mx:.4g} (oracle fp32-vs-fp64 spread {sp['max_abs']:.4g}, "
+         f"bound {SPREAD_MAX_FACTOR * sp['max_abs']:.4g}), p99.9 = {p999:.4g} (bound {TOL_BF16}), "
+         f"mean = {float(err.mean()):.3g}")
+    assert p999 <= TOL_BF16, f"{label}: p99.9 |dlogit| {p999} above {TOL_BF16}"
+    assert mx <= SPREAD_MAX_FACTOR * sp["max_abs"], f"{label}: max |dlogit| {mx}"
 
 
-@functools.lru_cache(maxsize=1)
+@functools.lru_cache(maxsize=3)
 def host_workload(name: str):
-    """(model with draft head, hidden) of a named workload; the last one is
-    kept so consecutive tests of a workload generate it once."""
+    """(model with draft head, hidden) of a named workload; the last three
+    are kept, so the forward and the step tests of a workload generate it
+    once (at most ~8 GB of bf16 host arrays)."""
     w = workload.WORKLOADS[name]
     note(f"{name}: generating weights")
     return workload.make_model(w), workload.make_hidden(w)
+
+
+@functools.lru_cache(maxsize=1)
+def oracle_step_logits(name: str):
+    """The oracle's target and draft logits [M, V] (fp64) on every row of a
+    named workload's step (the draft head reads the target's final hidden
+    state); kept for the last workload asked for."""
+    model, hidden = host_workload(name)
+    note(f"{name}: oracle forward on all {hidden.shape[0]} rows")
+    return oforward.forward(model, hidden, heads=("w_head", "w_draft_head"))

@@ -5,9 +5,10 @@ inputs, fp32 accumulation) and 1e-4 for the fp32 stack.  At full sizes the
 GPU computes every row in the same launch configuration the benchmark times;
 the oracle recomputes a sample of rows one by one.  Stacks truncated to 0, 1
 and 2 blocks at full width and vocabulary are held to 2e-2 strictly; the full
-stacks to the tolerance from full_stack_tol (the stated 2e-2, widened to 1.5x
-the spread that accumulation order alone produces through the random stack,
-measured on the oracle and stored under tests/golden/).
+stacks (check_full_stack) hold 2e-2 on 99.9% of the logits, and their maximum
+to 1.1x the spread that accumulation order alone produces through the random
+stack (measured on the oracle over every row of the step and stored under
+tests/golden/).  The step tests compare the full stacks on every row.
 """
 import numpy as np
 import pytest
@@ -15,8 +16,8 @@ import torch
 
 import workload
 from oracle import forward as of
-from tests.gpu_helpers import (TOL_BF16, TOL_F32, cpu, device_model, full_stack_tol, gpu,
-                               host_workload, note, require_gpu, spread_mean, to_dev_weight)
+from tests.gpu_helpers import (TOL_BF16, TOL_F32, check_full_stack, cpu, device_model, gpu,
+                               host_workload, note, require_gpu, to_dev_weight)
 
 
 def _check(gpu_rows, ref_rows, tol, label):
@@ -156,10 +157,12 @@ def _full_size(name, rows):
         m = sv.Model.packed(d_up[:L], d_down[:L], gain, d_head)    # the benchmark's layout
         z = cpu(m.forward(hid))
         ref = of.forward(of.truncated(model, L), hidden[rows])
-        tol = TOL_BF16 if L < w.n_layers else full_stack_tol(name)
-        err = _check(z[rows], ref, tol, f"{name} L={L} rows {rows}")
-        if L == w.n_layers:
-            assert err.mean() <= 1.5 * spread_mean(name)
+        label = f"{name} L={L} rows {rows}"
+        assert np.all(np.isfinite(z[rows]))
+        if L < w.n_layers:
+            _check(z[rows], ref, TOL_BF16, label)
+        else:
+            check_full_stack(np.abs(z[rows].astype(np.float64) - ref), name, label)
 
 
 @gpu

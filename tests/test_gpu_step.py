@@ -1,11 +1,21 @@
 """GPU parity of the whole verification step (spec_verify_step).
 
-Inputs: target weights and hidden states from ``workload``; draft logits and
-draft tokens from the oracle (the draft head reads the target's final hidden
-state).  The GPU step computes its own target logits, which differ from the
-oracle's by the forward tolerance; a request is compared bit for bit unless
-its oracle decisions lie within the band that the measured logit difference
-can move (derived in tests/gpu_helpers.step_band_near).
+Inputs: target weights and hidden states from ``workload``; draft logits are
+the oracle's draft-head logits on every row (the draft head reads the
+target's final hidden state) and draft tokens come from the oracle's sampler.
+
+Full-step token parity (publishertech section 2 "Modified Rejection
+Sampling"): the oracle's rejection sampling is run on the step's OWN logits
+(the fp32 logits the GPU step wrote, as fp64), with the same draft logits,
+draft tokens, seed and step, and every request must match bit for bit except
+those with a decision inside the stated 1e-5 band (|u - p/q| < 1e-5, or a
+replacement / bonus draw within 1e-5 R of a CDF boundary).  At the full
+vocabularies about half of the draws land inside that band (the emitted
+token's own mass is itself ~1e-5 of R), so each case asserts a minimum
+compared fraction and prints its counts.  The step's logits are checked
+against the oracle's on every row (check_full_stack); the end-to-end
+comparison (oracle logits -> oracle accept) is logged only, since a logit
+difference within tolerance legitimately moves decisions near a threshold.
 """
 import numpy as np
 import pytest
@@ -13,73 +23,91 @@ import torch
 
 import workload
 from oracle import forward as of, verify as ov
-from tests.gpu_helpers import (compare_accept, cpu, device_model, full_stack_tol, gpu,
-                               host_workload, note, require_gpu, step_band_near)
+from tests.gpu_helpers import (TOL_F32, check_full_stack, compare_accept, cpu, device_model, gpu,
+                               host_workload, note, oracle_step_logits, require_gpu)
+
+# minimum fraction of requests compared bit for bit (outside the 1e-5 band)
+MIN_COMPARED_SAMPLING = 0.35
+MIN_COMPARED_GREEDY = 1.0
 
 
-def _step_case(name, requests, T=None, step=0, seed=0):
+def _full_step(name, steps, T=None, seed=0):
+    """Runs the step for every (seed, step) in `steps` over all B requests and
+    returns (compared, total)."""
     sv = require_gpu()
     w = workload.WORKLOADS[name]
     T = w.temperature if T is None else T
     B, K, V = w.B, w.K, w.vocab
     model, hidden = host_workload(name)
-    rows = [b * (K + 1) + j for b in requests for j in range(K + 1)]
-    note(f"{name}: oracle forward on requests {requests}")
-    zt_ref, zd_ref = of.forward(model, hidden[rows], heads=("w_head", "w_draft_head"))
-    zt_ref = zt_ref.reshape(len(requests), K + 1, V)
-    zd_ref = zd_ref.reshape(len(requests), K + 1, V)[:, :K]
-    # draft inputs: oracle values for the checked requests, plain filler elsewhere
-    dl = np.zeros((B, K, V), np.float32)
-    dl[requests] = zd_ref.astype(np.float32)
-    x = workload.make_random_tokens(B, K, V, seed=seed)
-    x[requests] = ov.sample_draft_tokens(dl[requests], T, seed, step)
-
+    zt_ref, zd_ref = oracle_step_logits(name)
+    dl = np.ascontiguousarray(zd_ref.reshape(B, K + 1, V)[:, :K]).astype(np.float32)
+    dl64 = dl.astype(np.float64)
     m = device_model(sv, model, tiled=w.wdtype == "bf16")
-    logits, out, al = m.step(torch.from_numpy(hidden).cuda(), torch.from_numpy(dl).cuda(),
-                             torch.from_numpy(x).cuda(), B, K, T, seed, step)
-    torch.cuda.synchronize()
-    z_gpu = cpu(logits).reshape(B, K + 1, V)
-    out, al = cpu(out), cpu(al)
-    assert np.all((al >= 1) & (al <= K + 1))
-
-    tl_ref = np.zeros((B, K + 1, V))
-    tl_ref[requests] = zt_ref
-    dl_ref = dl.astype(np.float64)
-    ref_out, ref_al, res = ov.verify(tl_ref, dl_ref, x, T, seed, step, requests=requests)
-    set_aside = 0
-    for i, b in enumerate(requests):
-        eps = float(np.max(np.abs(z_gpu[b] - zt_ref[i])))
-        assert eps <= full_stack_tol(name), f"logits of request {b} off by {eps}"
-        if step_band_near(res[b], eps, T, zt_ref[i]):
-            set_aside += 1
-            continue
-        compare_accept(out, al, ref_out, ref_al, res, requests=[b])
-    note(f"{name}: {len(requests) - set_aside}/{len(requests)} requests bit-exact, "
-         f"{set_aside} inside the band; AL = {al[requests].tolist()}")
-    return al
+    hid_t, dl_t = torch.from_numpy(hidden).cuda(), torch.from_numpy(dl).cuda()
+    compared = total = e2e_agree = 0
+    checked_logits = False
+    for step in steps:
+        x = ov.sample_draft_tokens(dl, T, seed, step)
+        note(f"{name}: GPU step, T={T} seed={seed} step={step}, B={B} K={K} V={V}")
+        logits, out, al = m.step(hid_t, dl_t, torch.from_numpy(x).cuda(), B, K, T, seed, step)
+        torch.cuda.synchronize()
+        z_gpu = cpu(logits)
+        out, al = cpu(out), cpu(al)
+        assert np.all(np.isfinite(z_gpu))
+        assert np.all((al >= 1) & (al <= K + 1)), al
+        if not checked_logits:
+            err = np.abs(z_gpu.astype(np.float64) - zt_ref)
+            if w.wdtype == "bf16":
+                check_full_stack(err, name, f"{name} step logits, all {B * (K + 1)} rows")
+            else:
+                assert err.max() <= TOL_F32, err.max()
+            checked_logits = True
+        # the oracle's rejection sampling on the step's own logits
+        zg = z_gpu.astype(np.float64).reshape(B, K + 1, V)
+        ref_out, ref_al, res = ov.verify(zg, dl64, x, T, seed, step)
+        near = compare_accept(out, al, ref_out, ref_al, res)
+        compared += B - near
+        total += B
+        # logged only: the oracle end to end (its own logits)
+        e_out, e_al, _ = ov.verify(zt_ref.reshape(B, K + 1, V), dl64, x, T, seed, step)
+        agree = int(sum(al[b] == e_al[b] and np.array_equal(out[b], e_out[b]) for b in range(B)))
+        e2e_agree += agree
+        note(f"  step {step}: {B - near}/{B} requests bit-exact on the step's logits, {near} inside "
+             f"the 1e-5 band; end to end (oracle logits) {agree}/{B} agree; "
+             f"mean AL {al.mean():.3f}")
+    note(f"{name} T={T}: {compared}/{total} compared bit for bit ({compared / total:.0%}); "
+         f"end to end {e2e_agree}/{total}")
+    return compared, total
 
 
 @gpu
 def test_tiny_fp32_step():
-    _step_case("tiny-fp32", [0])
-    for s in range(1, 6):
-        _step_case("tiny-fp32", [0], step=s)
+    c, t = _full_step("tiny-fp32", range(8))
+    assert c >= MIN_COMPARED_SAMPLING * t
 
 
 @gpu
 def test_8b_shaped_b1k4_step():
-    _step_case("8b-shaped-b1-k4", [0])
+    c, t = _full_step("8b-shaped-b1-k4", range(32))
+    assert c >= MIN_COMPARED_SAMPLING * t
 
 
 @gpu
-@pytest.mark.parametrize("T", [1.0, 0.0])
-def test_70b_share_step(T):
-    _step_case("70b-layer-share-b8-k4", [0, 3, 7], T=T)
+def test_70b_share_step_sampling():
+    c, t = _full_step("70b-layer-share-b8-k4", range(4), T=1.0)
+    assert c >= MIN_COMPARED_SAMPLING * t
+
+
+@gpu
+def test_70b_share_step_greedy():
+    c, t = _full_step("70b-layer-share-b8-k4", range(2), T=0.0)
+    assert c >= MIN_COMPARED_GREEDY * t
 
 
 @gpu
 def test_large_batch_step():
-    _step_case("large-batch-b256-k2", [0, 128, 255])
+    c, t = _full_step("large-batch-b256-k2", range(1))
+    assert c >= MIN_COMPARED_SAMPLING * t
 
 
 @gpu

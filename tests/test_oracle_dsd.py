@@ -89,6 +89,8 @@ def test_ties_go_to_the_shorter_draft():
     ([1] * 9 + [0, 0, 1], 2),           # invalid (0) entries are skipped
 ])
 def test_window_rule(history, expect):
-    """publishertech section 5: below 1.5 over the last 10 requests the
-    window drops from 5 to a small value."""
+    """mohashari "Speculative Decoding in Production", "Production Failure
+    Modes and Mitigation Strategies", item 1 "Draft Acceptance Rate Collapse
+    (Entropy Shift)": below 1.5 over the last 10 requests the window drops
+    from 5 to a small value."""
     assert dsd.window_k(history, 10, 1.5, 5, 2) == expect

@@ -115,3 +115,19 @@ def test_draft_head_sigma_zero_equals_target():
     hidden = workload.make_hidden(wl)
     zt, zd = of.forward(model, hidden, heads=("w_head", "w_draft_head"))
     assert np.array_equal(zt, zd)
+
+
+def test_fp32_summation_orders_change_only_rounding():
+    """The fp32 evaluation in any summation order stays within fp32 rounding
+    of the fp64 reference on an fp32 stack (no bf16 rounding points), and
+    different orders really are different rounding sequences."""
+    w = workload.WORKLOADS["tiny-fp32"]
+    model = workload.make_model(w, draft_head=False)
+    h = workload.make_hidden(w, 6, sub=6)
+    z64 = of.forward(model, h)
+    zs = [of.forward(model, h, accum="f32", k_order=o) for o in (0, 1, 2)]
+    for z in zs:
+        assert np.abs(z - z64).max() <= 1e-4
+    assert not np.array_equal(zs[0], zs[1]) and not np.array_equal(zs[1], zs[2])
+    with pytest.raises(ValueError):
+        of.forward(model, h, k_order=1)

@@ -247,3 +247,27 @@ def test_planted_mistake_ignoring_temperature_is_caught(monkeypatch):
     obs = {k: v for k, v in obs.items() if k in law}
     n = sum(obs.values())
     assert _chi2(obs, law, n) < 1e-6
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 3.0])
+def test_softmax_matches_torch_fp64(T):
+    """softmax(z / T) (publishertech section 2 "Modified Rejection Sampling":
+    p and q are the models' next-token distributions at temperature T)
+    against torch.softmax in float64, an independent library routine, on
+    logits of several scales and with a large common offset; the oracle's
+    form subtracts the maximum first, so it must also be invariant to a
+    shift of every logit by the same constant."""
+    import torch
+    g = np.random.default_rng(int(T * 10))
+    for V, scale in ((7, 1.0), (1001, 3.0), (32000, 1.28), (4096, 20.0)):
+        z = g.standard_normal((3, V)) * scale
+        ref = torch.softmax(torch.from_numpy(z) / T, dim=-1).numpy()
+        got = ov.softmax(z, T)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
+        assert np.allclose(got.sum(-1), 1.0, rtol=0, atol=1e-12)
+        shifted = ov.softmax(z + 1234.5, T)
+        assert np.allclose(shifted, got, rtol=1e-9, atol=1e-300)
+    # one dominant logit at a low temperature: nearly one-hot, as torch has it
+    z = np.array([0.0, 5.0, 1.0, 5.0 - 1e-3])
+    assert np.allclose(ov.softmax(z, 0.01), torch.softmax(torch.from_numpy(z) / 0.01, -1).numpy(),
+                       rtol=1e-12, atol=1e-300)

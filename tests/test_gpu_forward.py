@@ -178,3 +178,21 @@ def test_70b_share_forward_sampled():
 @gpu
 def test_large_batch_forward_sampled():
     _full_size("large-batch-b256-k2", [0, 1, 2, 383, 765, 767])
+
+
+@gpu
+@pytest.mark.parametrize("tile", ["256", "192", "128", "64"])
+@pytest.mark.parametrize("M", [129, 200, 333])
+def test_lds_gemm_every_tile(tile, M, monkeypatch):
+    """The LDS-staged GEMM with each of its tiles forced (activation rows per
+    tile), at row counts with a ragged last tile, on a stack whose LM head
+    has a ragged vocabulary (V = 9001) and whose down projection splits its
+    4096-long reduction into fp32 partial planes."""
+    sv = require_gpu()
+    monkeypatch.setenv("SPEC_VERIFY_GEMM_TILE", tile)
+    w = workload.Workload("tiles-bf16", 512, 4096, 2, 9001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 7)
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w, M, sub=M)
+    z = cpu(m.forward(torch.from_numpy(h).cuda()))
+    _check(z, of.forward(model, h), TOL_BF16, f"LDS GEMM tile {tile} M={M}")

@@ -173,6 +173,29 @@ int spec_verify_accept(const float* target_logits, const float* draft_logits,
                        float* p_at_draft, float* q_at_draft,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* spec_verify_accept for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without the workspace.  Its
+ * scratch is one static device array of SV_ACCEPT_STATIC_SCRATCH_BYTES per
+ * GPU, held until the process ends.
+ *   - Sizes with spec_verify_accept_workspace_bytes(B, K, V) above that
+ *     limit return SV_ERR_WORKSPACE with nothing launched (4 MiB covers, for
+ *     instance, B = 1024, K = 8 at V = 128256: 2.9 MB).
+ *   - The first call on each device resolves the array's address
+ *     (hipGetSymbolAddress, with that device current) and keeps it; later
+ *     calls on that device reuse it.  The current device is the one used.
+ *   - Every call on a GPU shares that GPU's array: calls that overlap on one
+ *     GPU (two streams, or two threads) race, and the caller must order them.
+ *     Nothing in the array needs to start at zero.
+ *   - No device memory is allocated or freed; argument errors are reported as
+ *     for spec_verify_accept. */
+#define SV_ACCEPT_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+int spec_verify_accept_noalloc(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, int32_t B, int32_t K, int32_t V,
+                               float temperature, uint64_t seed, uint32_t step,
+                               int32_t* out_tokens, int32_t* accept_len,
+                               float* p_at_draft, float* q_at_draft, void* stream);
+
 /* The whole step: spec_verify_forward on hidden [B*(K+1), d] into
  * logits_out [B*(K+1), V], then spec_verify_accept on those logits with the
  * model's vocab.  ws >= spec_verify_workspace_bytes(m, B, K). */

@@ -57,6 +57,8 @@ EXPORTS = {
     "spec_verify_forward": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "spec_verify_accept": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float, _u64,
                                           _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_accept_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float,
+                                                  _u64, _u32, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _u64, _u32,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_last_error": (ctypes.c_char_p, []),
@@ -399,6 +401,27 @@ def accept(target_logits, draft_logits, draft_tokens, temperature: float, seed: 
                                     B, K, V, float(temperature), int(seed), int(step),
                                     _ptr(out_tokens), _ptr(accept_len), _ptr(p_at), _ptr(q_at),
                                     _ptr(ws), ws.numel(), _stream(stream)))
+    return out_tokens, accept_len
+
+
+def accept_noalloc(target_logits, draft_logits, draft_tokens, temperature: float, seed: int,
+                   step: int, out_tokens, accept_len, p_at=None, q_at=None, stream=None):
+    """``accept`` through the entry point that allocates nothing (its scratch is
+    the library's static per-device array): the outputs must be passed in."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    _need(target_logits, "target_logits", torch.float32, (B, K1, V))
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, (B, K, V))
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    _need(out_tokens, "out_tokens", torch.int32, (B, K1))
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _check(lib().spec_verify_accept_noalloc(_ptr(target_logits), _ptr(draft_logits),
+                                            _ptr(draft_tokens), B, K, V, float(temperature),
+                                            int(seed), int(step), _ptr(out_tokens),
+                                            _ptr(accept_len), _ptr(p_at), _ptr(q_at),
+                                            _stream(stream)))
     return out_tokens, accept_len
 
 

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "attn.hip", "cycle.hip", "gemm.hip", "kselect.cpp", "kvpool.cpp", "matmul.hip", "gemv.hip",
+SOURCES = ["accept_static.hip", "api.hip", "attn.hip", "cycle.hip", "gemm.hip", "kselect.cpp", "kvpool.cpp", "matmul.hip", "gemv.hip",
            "mfma.hip", "moe.hip", "norm.hip", "pack.hip", "vocab.hip"]
 ARCH = "gfx950"
 

@@ -197,8 +197,6 @@ int run_accept(const float* tl, const float* dl, const int32_t* x, int B, int K,
     return SV_OK;
 }
 
-namespace {
-
 int check_accept_args(const float* tl, const float* dl, const int32_t* x, int B, int K, int V,
                       float T, const int32_t* out, const int32_t* al) {
     if (B < 0 || K < 0 || V < 1)
@@ -213,6 +211,8 @@ int check_accept_args(const float* tl, const float* dl, const int32_t* x, int B,
     if (K > 0 && T > 0.0f && !dl) return fail(SV_ERR_INVALID_ARG, "null draft_logits with K > 0 and T > 0");
     return SV_OK;
 }
+
+namespace {
 
 // ---- per-launch timing -------------------------------------------------------
 struct ProfRec {

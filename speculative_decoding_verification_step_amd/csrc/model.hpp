@@ -34,5 +34,9 @@ int run_forward(const sv_model_desc& d, const float* hidden, int M, float* logit
 int run_accept(const float* tl, const float* dl, const int32_t* x, int B, int K, int V, float T,
                uint64_t seed, uint32_t step, int32_t* out, int32_t* al, float* p_at, float* q_at,
                char* ws, hipStream_t s);
+// Host checks of spec_verify_accept's arguments (sizes, temperature, null
+// pointers); SV_OK or the failure recorded for spec_verify_last_error.
+int check_accept_args(const float* tl, const float* dl, const int32_t* x, int B, int K, int V,
+                      float T, const int32_t* out, const int32_t* al);
 
 }  // namespace sv

@@ -123,6 +123,34 @@ def test_accept_rejects(L, kw, code):
     assert L.spec_verify_last_error()
 
 
+def _accept_noalloc(L, B=1, K=4, V=4096, T=1.0, tl=FAKE, dl=FAKE, x=FAKE, out=FAKE, al=FAKE):
+    return L.spec_verify_accept_noalloc(tl, dl, x, B, K, V, T, 0, 0, out, al, None, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), bd.SV_ERR_INVALID_ARG), (dict(K=-1), bd.SV_ERR_INVALID_ARG),
+    (dict(V=0), bd.SV_ERR_INVALID_ARG), (dict(T=float("nan")), bd.SV_ERR_INVALID_ARG),
+    (dict(tl=0), bd.SV_ERR_INVALID_ARG), (dict(x=0), bd.SV_ERR_INVALID_ARG),
+    (dict(dl=0), bd.SV_ERR_INVALID_ARG), (dict(out=0), bd.SV_ERR_INVALID_ARG),
+])
+def test_accept_noalloc_rejects(L, kw, code):
+    assert _accept_noalloc(L, **kw) == code
+    assert L.spec_verify_last_error()
+
+
+def test_accept_noalloc_scratch_limit(L):
+    """Sizes whose workspace exceeds the static scratch are refused on the
+    host (nothing launched, no device touched); the largest accepted size is
+    the one whose workspace still fits."""
+    limit = 4 << 20
+    assert L.spec_verify_accept_workspace_bytes(1024, 8, 128256) <= limit
+    assert L.spec_verify_accept_workspace_bytes(2048, 8, 128256) > limit
+    assert _accept_noalloc(L, B=2048, K=8, V=128256) == bd.SV_ERR_WORKSPACE
+    msg = L.spec_verify_last_error().decode()
+    assert "static scratch" in msg and str(limit) in msg
+    assert _accept_noalloc(L, B=0, tl=0, dl=0, x=0, out=0, al=0) == 0
+
+
 def test_accept_allows_null_draft_when_greedy_or_k0(L):
     # these pass the host checks; B = 0 keeps them from launching anything
     assert _accept(L, B=0, T=0.0, dl=0) == 0

@@ -147,3 +147,51 @@ def test_step_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(logits, ref[0]) and torch.equal(out, ref[1]) and torch.equal(al, ref[2])
         _ = (hidden * 2).sum().item()      # eager work between replays
+
+
+@gpu
+@pytest.mark.parametrize("V", [8960, 9001])
+@pytest.mark.parametrize("T", [1.0, 0.7, 0.0])
+def test_step_equals_forward_then_accept(V, T):
+    """From 65 rows the LM head runs on the LDS-staged GEMM.  The one-call
+    step must equal spec_verify_forward followed by spec_verify_accept on the
+    same logits bit for bit: logits, tokens, acceptance lengths, p(x) and
+    q(x), with and without a ragged last vocabulary tile.  With draft rows
+    equal to the target rows (p = q; publishertech section 2: the draft is
+    then accepted outright) every request accepts all K drafts."""
+    sv = require_gpu()
+    w = workload.Workload("step-vs-parts", 256, 768, 2, V, "bf16", 24, 3, 0.3, T, "std_0.02", 9)
+    B, K = w.B, w.K
+    M = B * (K + 1)
+    model = workload.make_model(w)
+    m = device_model(sv, model, tiled=True)
+    hidden = torch.from_numpy(workload.make_hidden(w)).cuda()
+    zt, zd = of.forward(model, workload.make_hidden(w), heads=("w_head", "w_draft_head"))
+    dl = np.ascontiguousarray(zd.reshape(B, K + 1, V)[:, :K]).astype(np.float32)
+    x = ov.sample_draft_tokens(dl, T, 5, 2)
+    dl_t, x_t = torch.from_numpy(dl).cuda(), torch.from_numpy(x).cuda()
+    for name, d_logits in (("draft head", dl_t), ("p = q", None)):
+        ref_logits = m.forward(hidden)
+        torch.cuda.synchronize()
+        if d_logits is None:
+            d_logits = ref_logits.view(B, K + 1, V)[:, :K].contiguous()
+            x_use = torch.from_numpy(ov.sample_draft_tokens(cpu(d_logits).astype(np.float64), T, 5, 2)).cuda()
+        else:
+            x_use = x_t
+        p_ref = torch.empty((B, K), device="cuda")
+        q_ref = torch.empty((B, K), device="cuda")
+        out_ref, al_ref = sv.accept(ref_logits.view(B, K + 1, V), d_logits if T > 0 else None, x_use, T,
+                                    5, 2, p_at=p_ref, q_at=q_ref)
+        p_st = torch.empty((B, K), device="cuda")
+        q_st = torch.empty((B, K), device="cuda")
+        logits, out, al = m.step(hidden, d_logits if T > 0 else None, x_use, B, K, T, 5, 2,
+                                 p_at=p_st, q_at=q_st)
+        torch.cuda.synchronize()
+        assert torch.equal(logits, ref_logits)
+        assert torch.equal(out, out_ref) and torch.equal(al, al_ref), name
+        if T > 0:
+            assert torch.equal(p_st.view(torch.int32), p_ref.view(torch.int32)), name
+            assert torch.equal(q_st.view(torch.int32), q_ref.view(torch.int32)), name
+        if name == "p = q":
+            assert torch.all(al == K + 1), cpu(al)
+        note(f"step vs forward + accept V={V} T={T} {name}: M={M}, identical; AL {cpu(al)[:8].tolist()}")

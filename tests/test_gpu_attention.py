@@ -66,6 +66,8 @@ CASES = [
     (1, 16, 64, 8, 128, [700], 24),              # 70B-shaped heads, K = 15: 8 tiles, split
     (2, 8, 8, 1, 128, [64, 500], 18),            # 4 tiles: the LDS-ring kernel, one tile per wave
     (1, 16, 16, 1, 64, [200], 8),                # 16 tiles: ring, four tiles per wave
+    (2, 16, 8, 1, 64, [1500, 40], 64),           # head_dim 64, two tiles per wave, 8 context splits
+    (1, 16, 16, 1, 64, [2000], 72),              # head_dim 64, four tiles per wave, 9 context splits
 ]
 
 

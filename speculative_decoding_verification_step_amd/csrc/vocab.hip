@@ -31,6 +31,7 @@
 // that holds the threshold always contains the drawn token.
 #include <float.h>
 #include <limits.h>
+#include <stdlib.h>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,6 +46,10 @@ constexpr int kPerThread = kChunk / kStatsThreads; // 32 = 8 float4
 constexpr int kRun = kPerThread;                   // consecutive ids per thread in a draw
 constexpr int kDrawThreads = kStatsThreads;
 constexpr int kMeta = 8;                           // per-request words passed to the draw
+// chunk workgroups from which the decisions are taken once per request: the
+// stage at B = 256, V = 128256 (4096 chunk workgroups) 199-201 -> 192-193 us;
+// at 128 (B = 8) and 4 (B = 1) workgroups the extra launch costs 1.4-1.7 us
+constexpr long long kSplitMinGroups = 1024;
 
 // exp(x) on the transcendental unit: v_exp_f32(x * log2(e)).  Relative error
 // about 2^-24 * |x * log2(e)| + 1 ulp, far inside the 1e-5 decision band for
@@ -421,6 +426,72 @@ __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
     }
 }
 
+// The same stage in two launches, for batches with many chunk workgroups
+// and for T = 0 (nothing to draw): decide_kernel takes each request's
+// decisions once (one workgroup per request) and leaves the draw parameters
+// in `meta`; chunk_total_kernel then only reads them and its chunk, where
+// decide_chunk_kernel repeats the decisions in every chunk workgroup.  Both
+// forms run the same functions on the same values, so their outputs are
+// bit-identical.
+__global__ __launch_bounds__(kDrawThreads) void decide_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft,
+    const int32_t* __restrict__ tokens, int K, int V, int nchunk, float inv_t, int greedy,
+    uint32_t k0, uint32_t k1, uint32_t step, const float* __restrict__ pv,
+    const float* __restrict__ ps, const int* __restrict__ pi, float* __restrict__ meta,
+    int32_t* __restrict__ out, int32_t* __restrict__ accept_len, float* __restrict__ p_at,
+    float* __restrict__ q_at, int B, int out_stride) {
+    const int b = blockIdx.x;
+    __shared__ int sh_first, sh_bad;
+    const size_t n_t = (size_t)B * (K + 1);
+    const int js = decide(target, draft, tokens, b, K, V, nchunk, inv_t, greedy, k0, k1, step, n_t,
+                          pv, ps, pi, true, p_at, q_at, &sh_first, &sh_bad);
+    float* mb = meta + (size_t)b * kMeta;
+    if (js < 0 || greedy) {
+        const int tok = js < 0 ? -1 : wave_row_argmax(pv, pi, (size_t)b * (K + 1) + js - 1, nchunk);
+        write_outputs(out, accept_len, tokens, b, K, js, tok, out_stride);
+        if (threadIdx.x == 0) mb[0] = __int_as_float(0);
+        return;
+    }
+    if (threadIdx.x < kWave) {
+        const size_t rt = (size_t)b * (K + 1) + js - 1;
+        const bool resid = js <= K;
+        const size_t rd = (size_t)b * K + js - 1;
+        float m, s;
+        wave_row_lse(pv, ps, rt, nchunk, inv_t, m, s);
+        float m2 = 0.f, s2 = 1.f;
+        if (resid) wave_row_lse(pv, ps, n_t + rd, nchunk, inv_t, m2, s2);
+        if (threadIdx.x == 0) {
+            mb[0] = __int_as_float(js);
+            mb[1] = m;
+            mb[2] = 1.0f / s;
+            mb[3] = resid ? m2 : 0.f;
+            mb[4] = resid ? 1.0f / s2 : 0.f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kDrawThreads) void chunk_total_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, int K, int V, int nchunk,
+    float inv_t, const float* __restrict__ meta, float* __restrict__ ctot) {
+    const int b = blockIdx.x / nchunk;
+    const int c = blockIdx.x - b * nchunk;
+    const float* mb = meta + (size_t)b * kMeta;
+    const int js = __float_as_int(mb[0]);
+    if (js <= 0) return;                       // no draw for this request
+    __shared__ float sh[kDrawThreads / kWave + 1];
+    const bool resid = js <= K;
+    DrawRows dr;
+    dr.zt = target + ((size_t)b * (K + 1) + js - 1) * V;
+    dr.zd = resid ? draft + ((size_t)b * K + js - 1) * V : nullptr;
+    dr.mt = mb[1];
+    dr.it_s = mb[2];
+    dr.md = mb[3];
+    dr.id_s = mb[4];
+    dr.inv_t = inv_t;
+    const float tot = chunk_total(dr, c, V, sh);
+    if (threadIdx.x == 0) ctot[(size_t)b * nchunk + c] = tot;
+}
+
 // Smallest y of chunk c with prefix + C_y > t (C as in run_sums / the block
 // scan); -1 if none.
 __device__ int find_in_chunk(const DrawRows& dr, int c, int V, float prefix, float t, float* sh,
@@ -568,7 +639,30 @@ hipError_t launch_accept(const float* target, const float* draft, const int32_t*
     const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
     float* ctot = scratch;
     float* meta = scratch + (size_t)B * nchunk;
-    {
+    // Decisions once per request (decide + chunk_total) when there are many
+    // chunk workgroups or nothing to draw (T = 0), else in every chunk
+    // workgroup (one launch).  SPEC_VERIFY_ACCEPT_SPLIT = 0 | 1 forces either
+    // form (tests, measurements).
+    bool split = greedy || (long long)B * nchunk >= kSplitMinGroups;
+    if (const char* e = getenv("SPEC_VERIFY_ACCEPT_SPLIT")) split = atoi(e) != 0;
+    if (split) {
+        {
+            ProfScope prof("decide", stream, 0.0, 0.0);
+            SV_LAUNCH(prof, decide_kernel, B, kDrawThreads, stream, target, draft, tokens, K, V,
+                      nchunk, inv_t, greedy, k0, k1, step, pv, ps, pi, meta, out_tokens,
+                      accept_len, p_at, q_at, B, K + 1);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (!greedy) {
+            // reads the draw rows once (two rows for a residual, one for a bonus)
+            ProfScope prof("chunk_total", stream, (double)B * 2.0 * V * 4.0, 0.0);
+            SV_LAUNCH(prof, chunk_total_kernel, B * nchunk, kDrawThreads, stream, target, draft, K,
+                      V, nchunk, inv_t, meta, ctot);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    } else {
         // reads the draw rows once (two rows for a residual, one for a bonus)
         ProfScope prof("decide_chunk", stream, greedy ? 0.0 : (double)B * 2.0 * V * 4.0, 0.0);
         SV_LAUNCH(prof, decide_chunk_kernel, B * nchunk, kDrawThreads, stream, target, draft,

@@ -172,3 +172,29 @@ def test_kernel_law_chi2(V, K, T):
     pv = chisquare(o2, e2 * o2.sum() / e2.sum()).pvalue
     note(f"chi2 V={V} K={K}: p = {pv:.3g}")
     assert pv > 1e-4
+
+
+@gpu
+@pytest.mark.parametrize("B,K,V,T", [(1, 4, 4096, 1.0), (24, 3, 9001, 0.7), (64, 4, 32000, 1.0),
+                                     (256, 2, 128256, 0.7), (8, 4, 128256, 0.0), (5, 0, 777, 0.8),
+                                     (3, 2, 1001, 3.0)])
+def test_split_and_fused_decisions_agree(B, K, V, T, monkeypatch):
+    """The stage's two launch forms -- decisions taken in every chunk
+    workgroup (one launch), or once per request and then the chunk totals
+    (two launches) -- run the same arithmetic on the same values, so they
+    agree bit for bit: tokens, acceptance lengths, p(x) and q(x)."""
+    sv = require_gpu()
+    t, d = workload.make_synthetic_logits(B, K, V, 1.3, 0.4, seed=11)
+    x = ov.sample_draft_tokens(d, T, 11, 2)
+    tt, dd, xx = torch.from_numpy(t).cuda(), torch.from_numpy(d).cuda(), torch.from_numpy(x).cuda()
+    got = {}
+    for mode in ("0", "1"):
+        monkeypatch.setenv("SPEC_VERIFY_ACCEPT_SPLIT", mode)
+        p_at = torch.full((B, K), float("nan"), dtype=torch.float32, device="cuda")
+        q_at = torch.full((B, K), float("nan"), dtype=torch.float32, device="cuda")
+        out, al = sv.accept(tt, dd if K else None, xx if K else None, T, 11, 2, p_at=p_at, q_at=q_at)
+        torch.cuda.synchronize()
+        got[mode] = (cpu(out), cpu(al), cpu(p_at).view(np.int32), cpu(q_at).view(np.int32))
+    for a, b in zip(got["0"], got["1"]):
+        assert np.array_equal(a, b)
+    note(f"split vs fused B={B} K={K} V={V} T={T}: identical; AL {got['1'][1][:8].tolist()}")

@@ -153,8 +153,8 @@ def test_kernel_law_chi2(V, K, T):
     law = laws.exact_outcome_law(p, q)
     x = np.stack([g.choice(V, size=n, p=q[j]) for j in range(K)], 1).astype(np.int32) if K else \
         np.zeros((n, 0), np.int32)
-    tt = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(zt, (n, K + 1, V)))).cuda()
-    dd = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(zd, (n, K, V)))).cuda()
+    tt = torch.from_numpy(np.broadcast_to(zt, (n, K + 1, V)).copy()).cuda()
+    dd = torch.from_numpy(np.broadcast_to(zd, (n, K, V)).copy()).cuda()
     out, al = sv.accept(tt, dd if K else None, torch.from_numpy(x).cuda() if K else None, T, 11, 5)
     out, al = cpu(out), cpu(al)
     keys = {}

@@ -79,8 +79,9 @@ hipError_t launch_rmsnorm_moe(float* h, const MoeFold& fold, const float* gain, 
 // measured on the 8B-shaped stack:
 //  - the projections stream their weights up to kTiledMinRows - 1 rows per
 //    pass and reuse them from LDS from kTiledMinRows on (LDS-staged GEMM);
-//    the LM head moves to the GEMM from kHeadTiledMinRows (57-61 vs 79 us
-//    streamed at 96-128 rows);
+//    the LM head moves to the GEMM from kHeadTiledMinRows (forward at 96 /
+//    128 rows: 0.624 / 0.662 ms against 0.635 / 0.680 with a streamed head;
+//    even at 80);
 //  - from kActTiledMinRows rows the activations are in the operand layout
 //    (one contiguous KiB per 16 rows x 32 k) for both families; below it they
 //    are row-major, where rows past M cost nothing (forward at 9 / 16 rows:

@@ -87,8 +87,10 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
     constexpr int BM32 = WM * FM;                // 32-row activation blocks per tile
     constexpr int NB = BN32 + BM32;
     constexpr int CP = 2 * NB;                   // 1 KiB operand copies per stage
-    static_assert(CP % NW == 0, "every wave issues the same number of copies");
-    constexpr int PER_WAVE = CP / NW;
+    // every wave issues PER_WAVE copies (so the vmcnt arithmetic is the same
+    // for all); when CP does not divide, the last ones repeat copy CP - 1
+    // (the same bytes to the same place)
+    constexpr int PER_WAVE = (CP + NW - 1) / NW;
     static_assert(PER_WAVE * (NS - 1) < 64, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS][CP * 512];
 
@@ -125,7 +127,7 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
     uint32_t coff[PER_WAVE];
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-        const int c = wave + NW * i;
+        const int c = min(wave + NW * i, CP - 1);
         const int half = c / NB, blk = c % NB;
         const int rb = blk < BN32 ? min(2 * (tn * BN32 + blk) + hi, nblk - 1)
                                   : min(2 * (tm * BM32 + blk - BN32) + hi, mblk - 1);
@@ -135,7 +137,7 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
         const int st = j % NS;
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
-            const int c = wave + NW * i;
+            const int c = min(wave + NW * i, CP - 1);
             const bool w = (c % NB) < BN32;
             copy_to_lds(w ? (const void*)Wt : (const void*)act, w ? bytes_w : bytes_a,
                         (lds_void*)(&lds[st][c * 512]), coff[i], j * 1024);
@@ -265,14 +267,20 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
 }
 
 // Tiles (WN x WM waves of FN x FM 32-row blocks; NS stages of k = 32), all
-// 256 weight rows wide (4 waves, one per SIMD, with up to 256 accumulator
-// registers each):
-//  T256 - 2 x 2 waves of 128 x 128: 256 activation rows, 4 stages of 32 KiB
-//  T192 - 2 x 2 waves of 128 x 96: 192 rows (768 rows in 4 tiles), 28 KiB stages
+// 256 weight rows wide:
+//  T256 - 2 x 2 waves of 128 x 128 (one per SIMD, 256 accumulator registers):
+//         256 activation rows, 4 stages of 32 KiB
+//  T192 - 4 x 2 waves of 64 x 96 (two per SIMD, 96 accumulators): 192 rows
+//         (768 rows in 4 tiles), 28 KiB stages.  More LDS reads per flop than
+//         2 x 2 waves of 128 x 96, but the second wave on each SIMD issues
+//         while the first waits: faster in 13 of 15 measured cases (up, down
+//         and head at 256-768 rows), e.g. up 93.9 -> 89.8 us and head 760.6 ->
+//         735.8 us at 768 rows.  (Eight waves of 128 x 64 on T256 lose on the
+//         head: 689.8 -> 701.4 us at 768 rows.)
 //  T128 - 2 x 2 waves of 128 x 64: 128 rows, 24 KiB stages
 //  T64  - 2 x 2 waves of 128 x 32: 64 rows, 20 KiB stages
 struct T256 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 4, NS = 4, WPE = 1; };
-struct T192 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 3, NS = 4, WPE = 1; };
+struct T192 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 3, NS = 4, WPE = 1; };
 struct T128 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 2, NS = 4, WPE = 1; };
 struct T64 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 1, NS = 5, WPE = 1; };
 

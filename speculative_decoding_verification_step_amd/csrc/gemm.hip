@@ -277,11 +277,15 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
 //         and head at 256-768 rows), e.g. up 93.9 -> 89.8 us and head 760.6 ->
 //         735.8 us at 768 rows.  (Eight waves of 128 x 64 on T256 lose on the
 //         head: 689.8 -> 701.4 us at 768 rows.)
-//  T128 - 2 x 2 waves of 128 x 64: 128 rows, 24 KiB stages
-//  T64  - 2 x 2 waves of 128 x 32: 64 rows, 20 KiB stages
+//  T128 - 4 x 2 waves of 64 x 64 (two per SIMD): 128 rows, 24 KiB stages;
+//         against 2 x 2 waves of 128 x 64 the up projection runs 4-10% faster
+//         at 144-640 rows (e.g. 72.3 -> 67.3 us at 512), down and head within
+//         2% either way
+//  T64  - 2 x 2 waves of 128 x 32: 64 rows, 20 KiB stages (eight waves of
+//         64 x 32 gain nothing)
 struct T256 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 4, NS = 4, WPE = 1; };
 struct T192 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 3, NS = 4, WPE = 1; };
-struct T128 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 2, NS = 4, WPE = 1; };
+struct T128 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 2, NS = 4, WPE = 1; };
 struct T64 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 1, NS = 5, WPE = 1; };
 
 template <class T> constexpr int tn32() { return T::WN * T::FN * 32; }

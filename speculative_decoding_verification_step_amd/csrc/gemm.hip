@@ -283,10 +283,10 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
 //         2% either way
 //  T64  - 2 x 2 waves of 128 x 32: 64 rows, 20 KiB stages (eight waves of
 //         64 x 32 gain nothing)
-struct T256 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 4, NS = 4, WPE = 1; };
-struct T192 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 3, NS = 4, WPE = 1; };
-struct T128 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 2, NS = 4, WPE = 1; };
-struct T64 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 1, NS = 5, WPE = 1; };
+struct T256 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 4, NS = 4, WPE = 1; static constexpr double EFF = 1.00; };
+struct T192 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 3, NS = 4, WPE = 1; static constexpr double EFF = 0.96; };
+struct T128 { static constexpr int WN = 4, WM = 2, FN = 2, FM = 2, NS = 4, WPE = 1; static constexpr double EFF = 0.87; };
+struct T64 { static constexpr int WN = 2, WM = 2, FN = 4, FM = 1, NS = 5, WPE = 1; static constexpr double EFF = 0.60; };
 
 template <class T> constexpr int tn32() { return T::WN * T::FN * 32; }
 template <class T> constexpr int tm32() { return T::WM * T::FM * 32; }
@@ -317,13 +317,13 @@ hipError_t launch32(const MatmulArgs& a, int splits, hipStream_t stream) {
 constexpr int kCUs = 256;       // one workgroup per CU (LDS and registers)
 constexpr int kMaxSplits = 8;
 
-// Relative efficiency of a tile: the bytes copied and read from LDS per flop
-// grow as 1/BM + 1/BN.  The weight 24 ranks the measured large-batch shapes
-// (768 rows): 192-row tiles for the projections (one round of 224 tiles
-// instead of 168 on 256 CUs), 256-row tiles for the 128256-row LM head.
-template <class T> constexpr double tile_eff() {
-    return 1.0 / (1.0 + 24.0 * (1.0 / tm32<T>() + 1.0 / tn32<T>()) - 24.0 * (2.0 / 256));
-}
+// Relative rate of a tile (output area per unit time, per workgroup), fitted
+// to every tile forced on the 8B-shaped projections and a 128256-row LM head
+// at 144-768 rows (medians over the three products): 256 rows 1.00, 192 rows
+// 0.96, 128 rows 0.87, 64 rows 0.60.  With these the choice is within 3% of
+// the fastest tile at 31 of those 33 points (7.5% at the other two), where
+// a 1/BM + 1/BN model lost 23% on the up projection at 576 rows.
+template <class T> constexpr double tile_eff() { return T::EFF; }
 
 // Cost of one tile choice: full rounds of kCUs workgroups x the k steps of
 // one split x the tile's area, over its efficiency.

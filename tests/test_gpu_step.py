@@ -195,3 +195,32 @@ def test_step_equals_forward_then_accept(V, T):
         if name == "p = q":
             assert torch.all(al == K + 1), cpu(al)
         note(f"step vs forward + accept V={V} T={T} {name}: M={M}, identical; AL {cpu(al)[:8].tolist()}")
+
+
+@gpu
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_step_without_drafts_and_empty_batch(T):
+    """K = 0 verifies only the bonus position: every request emits one token
+    drawn from its row's p (or its argmax at T = 0) and AL = 1, matching the
+    oracle's rejection sampling on the step's own logits.  B = 0 is a no-op."""
+    sv = require_gpu()
+    w = workload.Workload("k0-bf16", 256, 768, 2, 9001, "bf16", 6, 0, 0.3, T, "std_0.02", 21)
+    B, V = w.B, w.vocab
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w)
+    logits, out, al = m.step(torch.from_numpy(h).cuda(), None, None, B, 0, T, 3, 5)
+    torch.cuda.synchronize()
+    z, out, al = cpu(logits).astype(np.float64), cpu(out), cpu(al)
+    assert out.shape == (B, 1) and np.all(al == 1)
+    ref_out, ref_al, res = ov.verify(z.reshape(B, 1, V), np.zeros((B, 0, V)), np.zeros((B, 0), np.int32),
+                                     T, 3, 5)
+    near = compare_accept(out, al, ref_out, ref_al, res)
+    assert B - near >= (B if T == 0 else 1)
+    note(f"K = 0, T={T}: {B - near}/{B} bonus tokens bit-exact on the step's logits")
+    # an empty batch: nothing to do, nothing written
+    e_logits = torch.full((0, V), float("nan"), device="cuda")
+    e_out = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    e_al = torch.empty((0,), dtype=torch.int32, device="cuda")
+    m.step(torch.empty((0, w.d), device="cuda"), None, None, 0, 0, T, 3, 5, e_logits, e_out, e_al)
+    torch.cuda.synchronize()

@@ -177,7 +177,7 @@ def test_kernel_law_chi2(V, K, T):
 @gpu
 @pytest.mark.parametrize("B,K,V,T", [(1, 4, 4096, 1.0), (24, 3, 9001, 0.7), (64, 4, 32000, 1.0),
                                      (256, 2, 128256, 0.7), (8, 4, 128256, 0.0), (5, 0, 777, 0.8),
-                                     (3, 2, 1001, 3.0)])
+                                     (3, 2, 1001, 3.0), (8, 4, 128256, 1.0), (2, 16, 70000, 1.0)])
 def test_split_and_fused_decisions_agree(B, K, V, T, monkeypatch):
     """The stage's two launch forms -- decisions taken in every chunk
     workgroup (one launch), or once per request and then the chunk totals

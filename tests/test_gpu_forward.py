@@ -181,6 +181,31 @@ def test_large_batch_forward_sampled():
 
 
 @gpu
+@pytest.mark.parametrize("M", [448, 700])
+def test_large_batch_weights_ragged_rows(M):
+    """The large-batch stack (d = 4096, ffn = 14336, V = 128256, benchmark
+    layout) at row counts that leave a ragged last tile in every GEMM the
+    library picks there (eight-wave 192- and 128-row tiles, split down
+    projection, 256-row LM head), one and two blocks deep, on sampled rows at
+    the tile edges and the tail."""
+    sv = require_gpu()
+    w = workload.WORKLOADS["large-batch-b256-k2"]
+    model, hidden = host_workload("large-batch-b256-k2")
+    hidden = np.ascontiguousarray(hidden[:M])
+    rows = sorted({0, 63, 64, 127, 128, 191, 192, 255, 256, M // 2, M - 2, M - 1})
+    d_up, d_down = to_dev_weight(model["w_up"]), to_dev_weight(model["w_down"])
+    d_head = to_dev_weight(model["w_head"])
+    hid = torch.from_numpy(hidden).cuda()
+    for L in (1, 2):
+        gain = torch.ones((L + 1, w.d), dtype=torch.float32, device="cuda")
+        m = sv.Model.packed(d_up[:L], d_down[:L], gain, d_head)
+        z = cpu(m.forward(hid))
+        assert np.all(np.isfinite(z))
+        _check(z[rows], of.forward(of.truncated(model, L), hidden[rows]), TOL_BF16,
+               f"large-batch weights M={M} L={L} rows {rows}")
+
+
+@gpu
 @pytest.mark.parametrize("tile", ["256", "192", "128", "64"])
 @pytest.mark.parametrize("M", [129, 200, 333])
 def test_lds_gemm_every_tile(tile, M, monkeypatch):

@@ -281,14 +281,43 @@ def _time_step(sv, target, hidden, zq, x, B, K, T, steps, warmup, use_graph, see
     return ms, wall, per, (logits, out, al, ws, s, one)
 
 
-def _profile_kernels(sv, one, s, reps):
+PROFILE_REPS = 20
+PROFILE_BACKLOG_MS = 8.0
+PROFILE_MAX_LAUNCHES_PER_STEP = 64
+
+
+def _profile_backlog_steps(step_ms: float) -> int:
+    """Untimed steps queued ahead of each timed one: about
+    PROFILE_BACKLOG_MS of GPU work, at least 2."""
+    return int(min(200, max(2, math.ceil(PROFILE_BACKLOG_MS / max(step_ms, 1e-3)))))
+
+
+def _profile_kernels(sv, one, s, step_ms, reps=PROFILE_REPS):
+    """Per-kernel times from HIP events that each dispatch records at its own
+    start and end, over `reps` steps.  Events on every dispatch slow the step
+    by about 5 % on the 768-row workload, so they stay out of the timed loop.
+    A launch with events also costs the host more than a short kernel takes
+    to run, so each timed step is queued behind a backlog of untimed steps
+    (profiling paused; about PROFILE_BACKLOG_MS of GPU work): the GPU reaches
+    the timed step busy, at the clock of the timed loop, with the step's
+    launches already queued, and runs them back to back as in the timed loop
+    instead of waiting on the host.  Returns the per-kernel table and the
+    backlog per timed step."""
     import torch
-    sv.profile_begin(1 << 16)
-    with torch.cuda.stream(s):
-        for _ in range(reps):
-            one()
-    torch.cuda.synchronize()
-    return sv.profile_end(64)
+    backlog = _profile_backlog_steps(step_ms)
+    sv.profile_begin(reps * PROFILE_MAX_LAUNCHES_PER_STEP)
+    try:
+        with torch.cuda.stream(s):
+            for _ in range(reps):
+                sv.profile_pause(True)
+                for _ in range(backlog):
+                    one()
+                sv.profile_pause(False)
+                one()
+        torch.cuda.synchronize()
+    finally:
+        kt = sv.profile_end(64)
+    return kt, backlog
 
 
 def _cpu_model() -> str:
@@ -454,7 +483,7 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
              other_per[(9 * len(other_per)) // 10]],
     }
     if profile:
-        kt = _profile_kernels(sv, one, s, reps=5)
+        kt, backlog = _profile_kernels(sv, one, s, ms)
         dom = max(kt, key=lambda k: kt[k][1])
         n, tot, b, f = kt[dom]
         avg_s = tot / n / 1e3
@@ -475,8 +504,11 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
         roof["algorithmic_bytes_per_launch"] = b / n
         roof["algorithmic_flops_per_launch"] = f / n
         res["roofline"] = roof
-        res["kernels"] = {k: {"launches": v[0] // 5, "ms_per_step": v[1] / 5,
+        res["kernels"] = {k: {"launches": v[0] // PROFILE_REPS, "ms_per_step": v[1] / PROFILE_REPS,
                               "gbs": v[2] / max(v[1], 1e-9) / 1e6} for k, v in kt.items()}
+        res["kernels_profile_steps"] = PROFILE_REPS
+        res["kernels_profile_backlog_steps"] = backlog
+        res["kernels_ms_per_step_sum"] = sum(v[1] for v in kt.values()) / PROFILE_REPS
     if cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline(host, w, B, K, T, 0)
     del target, hidden, zq, x, logits, out, al, ws

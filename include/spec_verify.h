@@ -230,6 +230,13 @@ typedef struct {
 int spec_verify_profile_begin(int32_t max_launches);
 int spec_verify_profile_end(sv_kernel_time* out, int32_t cap, int32_t* n_out);
 
+/* Between profile_begin and profile_end: paused != 0 stops recording (later
+ * launches run untimed and take no slot), 0 resumes it.  A launch with events
+ * costs the host more than a short kernel takes to run, so a caller can queue
+ * untimed work ahead of each timed step and keep the GPU from waiting on the
+ * host inside the timed launches.  SV_ERR_INVALID_ARG when profiling is off. */
+int spec_verify_profile_pause(int32_t paused);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,6 @@ from .binding import (  # noqa: F401
     KV_BLOCK, KVPool, LIB_PATH, Model, MoEModel, SpecVerifyError, accept, accept_noalloc,
     accept_workspace_bytes, attention,
     attention_workspace_bytes, choose_k, cycle, cycle_workspace_bytes, embed, kv_append, kv_commit,
-    lib, pack, profile_begin, profile_end, sample, sample_workspace_bytes, window_k, workspace,
+    lib, pack, profile_begin, profile_end, profile_pause, sample, sample_workspace_bytes, window_k, workspace,
     SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP,
 )

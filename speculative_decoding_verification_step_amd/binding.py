@@ -63,6 +63,7 @@ EXPORTS = {
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_last_error": (ctypes.c_char_p, []),
     "spec_verify_profile_begin": (ctypes.c_int, [_i32]),
+    "spec_verify_profile_pause": (ctypes.c_int, [_i32]),
     "spec_verify_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), _i32,
                                                ctypes.POINTER(_i32)]),
     "spec_verify_choose_k": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
@@ -427,6 +428,10 @@ def accept_noalloc(target_logits, draft_logits, draft_tokens, temperature: float
 
 def profile_begin(max_launches: int = 65536):
     _check(lib().spec_verify_profile_begin(max_launches))
+
+
+def profile_pause(paused: bool):
+    _check(lib().spec_verify_profile_pause(1 if paused else 0))
 
 
 def profile_end(cap: int = 64):

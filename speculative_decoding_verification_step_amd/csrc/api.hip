@@ -223,6 +223,7 @@ struct ProfRec {
 struct ProfState {
     std::mutex mu;
     std::atomic<bool> on{false};
+    bool paused = false;
     int cap = 0;
     std::vector<hipEvent_t> ev;
     std::vector<ProfRec> recs;
@@ -240,7 +241,7 @@ ProfScope::ProfScope(const char* name, hipStream_t s, double bytes, double flops
     ProfState& p = prof();
     if (!p.on) return;
     std::lock_guard<std::mutex> g(p.mu);
-    if (!p.on || (int)p.recs.size() >= p.cap) return;
+    if (!p.on || p.paused || (int)p.recs.size() >= p.cap) return;
     const size_t slot = p.recs.size();
     p.recs.push_back({name, bytes, flops});
     ev0 = p.ev[2 * slot];
@@ -415,7 +416,16 @@ int spec_verify_profile_begin(int32_t max_launches) {
     p.recs.clear();
     p.recs.reserve(max_launches);
     p.cap = max_launches;
+    p.paused = false;
     p.on = true;
+    return SV_OK;
+}
+
+int spec_verify_profile_pause(int32_t paused) {
+    ProfState& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.on) return fail(SV_ERR_INVALID_ARG, "profiling not on");
+    p.paused = paused != 0;
     return SV_OK;
 }
 

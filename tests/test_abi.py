@@ -193,6 +193,8 @@ def test_forward_and_step_reject(L):
 def test_profile_state_machine(L):
     assert L.spec_verify_profile_end(None, 0, None) == bd.SV_ERR_INVALID_ARG
     assert L.spec_verify_profile_begin(0) == bd.SV_ERR_INVALID_ARG
+    assert L.spec_verify_profile_pause(1) == bd.SV_ERR_INVALID_ARG     # profiling is off
+    assert L.spec_verify_profile_pause(0) == bd.SV_ERR_INVALID_ARG
 
 
 def test_packed_sizes_and_pack_rejects(L):

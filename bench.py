@@ -691,18 +691,17 @@ def _attention_bench(a):
             scale = 1.0 / math.sqrt(Dh)
             ms = _time_fn(lambda s: sv.attention(q, kc, vc, table, ctx_len, scale, out=out, ws=ws,
                                                  stream=s), 50, 5, a.graph)
-            sv.profile_begin(1 << 12)
-            for _ in range(5):
+            def one_call():
                 sv.attention(q, kc, vc, table, ctx_len, scale, out=out, ws=ws)
                 sv.kv_append(kn, vn, kc, vc, table, ctx_len)
-            torch.cuda.synchronize()
-            kt = sv.profile_end(16)
+
+            kt, _ = _profile_kernels(sv, one_call, torch.cuda.Stream(), ms)
             kv_bytes = B * Hkv * (ctx + T) * Dh * 2 * 2
             io_bytes = B * T * Hq * Dh * (2 + 4)
             flops = 4.0 * B * Hq * T * (ctx + (T + 1) / 2.0) * Dh
-            main = kt.get("attention", (5, 5 * ms, 0, 0))
+            main = kt.get("attention", (PROFILE_REPS, PROFILE_REPS * ms, 0, 0))
             comb = kt.get("attention_combine", (0, 0.0, 0, 0))
-            app = kt.get("kv_append", (5, 0.0, 0, 0))
+            app = kt.get("kv_append", (PROFILE_REPS, 0.0, 0, 0))
             comb_us = comb[1] / comb[0] * 1e3 if comb[0] else 0.0
             attn_us = main[1] / main[0] * 1e3 + comb_us    # both launches of one call
             res = {"attention": name, "B": B, "Hq": Hq, "Hkv": Hkv, "G": G, "Dh": Dh, "ctx": ctx,

@@ -386,41 +386,92 @@ def _cpu_baseline(host, w, B, K, T, seed):
 _CEILINGS: dict = {}
 
 
-def practical_ceiling(bound: str):
-    """A measured practical ceiling for an MFMA-bound roofline, beside the
-    published peak, taken once per process after the timed work: torch.matmul
-    in bf16 (hipBLASLt) on a large product, 16384 x 16384 x 8192 with random
-    operands; median of 5 timed calls after 2 untimed.  None for other bounds
-    (torch's reductions and copies stream slower than the weight-streaming
-    kernels here, so they are no ceiling for them)."""
+CEILING_WARM_MS = 60.0
+CEILING_TIMED_MS = 40.0
+CEILING_ROTATE_BYTES = 1.0e9     # beyond the 256 MB last-level cache
+
+
+def _time_back_to_back(fn, est_ms):
+    """Average ms per call of fn(i) over calls queued back to back on one
+    stream: about CEILING_WARM_MS of untimed calls first (the GPU reaches the
+    timed calls busy, at its loaded clock), then about CEILING_TIMED_MS of
+    calls between one pair of events."""
     import torch
-    if bound != "mfma":
-        return None
-    if bound in _CEILINGS:
-        return _CEILINGS[bound]
     s = torch.cuda.Stream()
-    gen = torch.Generator(device="cuda").manual_seed(0)
-    m, n, k = 16384, 16384, 8192
-    a = torch.randn((m, k), device="cuda", generator=gen).to(torch.bfloat16)
-    b = torch.randn((k, n), device="cuda", generator=gen).to(torch.bfloat16)
-    fn, work, unit = (lambda: torch.matmul(a, b)), 2.0 * m * n * k / 1e12, "TFLOP/s"
-    what = "torch.matmul bf16 16384x16384x8192 (hipBLASLt), random operands, same run"
+    warm = int(min(2000, max(3, math.ceil(CEILING_WARM_MS / est_ms))))
+    n = int(min(2000, max(5, math.ceil(CEILING_TIMED_MS / est_ms))))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    times = []
     with torch.cuda.stream(s):
-        for i in range(7):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            fn()
-            e1.record(s)
-            e1.synchronize()
-            if i >= 2:
-                times.append(e0.elapsed_time(e1) / 1e3)
-    times.sort()
-    _CEILINGS[bound] = {"value": work / times[len(times) // 2], "unit": unit, "what": what}
-    del s
+        for i in range(warm):
+            fn(i)
+        e0.record(s)
+        for i in range(n):
+            fn(i)
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, n
+
+
+def _weight_shape(w, label: str):
+    """[out, in] of the weight a forward launch streams, by its label."""
+    if label.endswith("up_silu"):
+        return w.ffn, w.d
+    if label.endswith("down_residual"):
+        return w.d, w.ffn
+    if label.endswith("head"):
+        return w.vocab, w.d
+    return None
+
+
+def practical_ceiling(bound: str, w=None, M: int = 0, label: str = ""):
+    """A measured practical ceiling beside the published peak, taken once per
+    process and shape after the timed work, with the vendor BLAS (hipBLASLt
+    through torch) on random bf16 operands, calls queued back to back.
+    MFMA-bound: torch.matmul 16384 x 16384 x 8192.  HBM-bound (bf16 weights):
+    the dominant launch's own product, F.linear of [M, in] activations with
+    its [out, in] weight (no epilogue), the weight rotated over enough copies
+    (>= 1 GB) that no call finds it in the last-level cache; rate = (weight +
+    activations + output bytes) / time, the same count as the library's own
+    weight-streaming roofline."""
+    import torch
+    import torch.nn.functional as F
+    if bound == "mfma":
+        key = ("mfma",)
+    elif bound == "hbm" and w is not None and w.wdtype == "bf16" and M > 0 \
+            and _weight_shape(w, label):
+        key = ("hbm", M) + _weight_shape(w, label)
+    else:
+        return None
+    if key in _CEILINGS:
+        return _CEILINGS[key]
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    if bound == "mfma":
+        m, n, k = 16384, 16384, 8192
+        a = torch.randn((m, k), device="cuda", generator=gen).to(torch.bfloat16)
+        b = torch.randn((k, n), device="cuda", generator=gen).to(torch.bfloat16)
+        ms, calls = _time_back_to_back(lambda i: torch.matmul(a, b), 3.5)
+        res = {"value": 2.0 * m * n * k / (ms / 1e3) / 1e12, "unit": "TFLOP/s",
+               "what": f"torch.matmul bf16 16384x16384x8192 (hipBLASLt), random operands, "
+                       f"{calls} calls back to back, same run"}
+        del a, b
+    else:
+        n_out, n_in = _weight_shape(w, label)
+        wbytes = n_out * n_in * 2
+        copies = max(1, math.ceil(CEILING_ROTATE_BYTES / wbytes))
+        ws = [(torch.randn((n_out, n_in), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+              for _ in range(copies)]
+        x = torch.randn((M, n_in), device="cuda", generator=gen).to(torch.bfloat16)
+        nbytes = wbytes + M * n_in * 2 + M * n_out * 2
+        ms, calls = _time_back_to_back(lambda i: F.linear(x, ws[i % copies]),
+                                       nbytes / (6e12) * 1e3)
+        res = {"value": nbytes / (ms / 1e3) / 1e9, "unit": "GB/s",
+               "what": f"torch F.linear bf16 [{M},{n_in}] x [{n_out},{n_in}]^T (vendor BLAS), weight "
+                       f"rotated over {copies} copies, {calls} calls back to back, same run"}
+        del ws, x
+    _CEILINGS[key] = res
     torch.cuda.empty_cache()
-    return _CEILINGS[bound]
+    return res
 
 
 def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile=True):
@@ -495,7 +546,7 @@ def run_point(w, B, K, sigma, T, steps, warmup, use_graph, cpu_baseline, profile
             roof = {"bound": "mfma", "achieved": f / n / avg_s / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        ceil = practical_ceiling(roof["bound"])
+        ceil = practical_ceiling(roof["bound"], w, M, dom)
         if ceil:
             roof["ceiling"] = dict(ceil, frac=roof["achieved"] / ceil["value"])
         roof["traffic"] = measured_traffic(w.name, dom) if (B, K) == (w.B, w.K) else None

@@ -25,6 +25,8 @@ CASES = [
     (256, 2, 128256, 0.7, 1.28, 0.64),     # large batch, T = 0.7
     (7, 3, 2053, 0.0, 1.0, 0.5),
     (4, 3, 3000, 3.0, 1.0, 2.0),           # high temperature: acceptance collapse
+    (3, 20, 5000, 1.0, 1.5, 0.2),          # long drafts: five positions per wave
+    (1024, 1, 4096, 1.0, 1.5, 0.4),        # many short requests: 1024 chunk groups, split form
 ]
 
 

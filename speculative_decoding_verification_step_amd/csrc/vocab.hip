@@ -24,11 +24,12 @@
 //                 sums the weights of the draw row over its chunk;
 //   draw          per request: prefix over the chunk sums, then rescans only
 //                 the chunk that holds u' * R.
-// Within a chunk, thread t owns the run of kRun consecutive ids starting at
-// kRun * t; the running sum C_y is prefix(chunk) + exclusive(thread) +
-// running sum within the run, and the chunk total is the last thread's
-// inclusive value, computed by the same code in both kernels, so the chunk
-// that holds the threshold always contains the drawn token.
+// Within a chunk a draw scan takes kPasses passes of kPassIds ids; in each,
+// thread t owns the run of 4 consecutive ids at 4t.  The running sum C_y is
+// prefix(chunk) + (earlier passes' totals + (exclusive(thread) + running sum
+// within the run)), and the chunk total is its value at the chunk's last id,
+// computed by the same code in both kernels, so the chunk that holds the
+// threshold always contains the drawn token.
 #include <float.h>
 #include <limits.h>
 #include <stdlib.h>
@@ -43,8 +44,10 @@ namespace {
 constexpr int kStatsThreads = 256;
 constexpr int kChunk = 8192;                       // logits per chunk workgroup
 constexpr int kPerThread = kChunk / kStatsThreads; // 32 = 8 float4
-constexpr int kRun = kPerThread;                   // consecutive ids per thread in a draw
 constexpr int kDrawThreads = kStatsThreads;
+constexpr int kPassIds = 4 * kDrawThreads;         // ids per pass of a draw scan: a float4 per thread
+constexpr int kPasses = kChunk / kPassIds;         // 8 passes per chunk
+constexpr int kScanShared = kPasses * (kDrawThreads / kWave + 1);   // floats of LDS per scan
 constexpr int kMeta = 8;                           // per-request words passed to the draw
 // chunk workgroups from which the decisions are taken once per request: the
 // stage at B = 256, V = 128256 (4096 chunk workgroups) 199-201 -> 192-193 us;
@@ -228,70 +231,120 @@ __device__ __forceinline__ float weight(const DrawRows& dr, int y) {
     return fmaxf(0.f, p - prob(dr.zd[y], dr.md, dr.inv_t, dr.id_s));
 }
 
-// The kRun weights of thread t's run in chunk c (zero past V), as running sums.
-__device__ __forceinline__ void run_sums(const DrawRows& dr, int c, int V, float run[kRun]) {
-    const int y0 = c * kChunk + kRun * threadIdx.x;
-    float w[kRun];
+// Draw weights of chunk c in kPasses passes of kPassIds ids.  In pass p,
+// thread t owns the run of 4 ids c * kChunk + p * kPassIds + 4t .. +3 (zero
+// past V), so the lanes of a load are 16 B apart and every line a wave
+// touches is read once.  run[p][i] holds the running sum over the run.
+__device__ __forceinline__ void pass_runs(const DrawRows& dr, int c, int V,
+                                          float run[kPasses][4]) {
+    const int y0 = c * kChunk + 4 * (int)threadIdx.x;
+    float w[kPasses][4];
     const bool vec = (V % 4 == 0) && ((uintptr_t)dr.zt % 16 == 0) &&
-                     (!dr.zd || (uintptr_t)dr.zd % 16 == 0) && y0 + kRun <= V;
+                     (!dr.zd || (uintptr_t)dr.zd % 16 == 0);
     if (vec) {
-        // whole run in range and 16-byte aligned: four vector loads per row
-        f32x4 zt[kRun / 4], zd[kRun / 4];
+        // V % 4 == 0: a run is wholly inside the row or wholly past it.  Runs
+        // past it load the row's last four values (no branch around the
+        // loads) and weigh zero.
+        f32x4 zt[kPasses], zd4[kPasses];
+        if (dr.zd) {
 #pragma unroll
-        for (int v = 0; v < kRun / 4; ++v) {
-            zt[v] = *reinterpret_cast<const f32x4*>(dr.zt + y0 + 4 * v);
-            if (dr.zd) zd[v] = *reinterpret_cast<const f32x4*>(dr.zd + y0 + 4 * v);
+            for (int p = 0; p < kPasses; ++p) {
+                const int y = min(y0 + p * kPassIds, V - 4);
+                zt[p] = *reinterpret_cast<const f32x4*>(dr.zt + y);
+                zd4[p] = *reinterpret_cast<const f32x4*>(dr.zd + y);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                zt[p] = *reinterpret_cast<const f32x4*>(dr.zt + min(y0 + p * kPassIds, V - 4));
+                zd4[p] = zt[p];
+            }
         }
 #pragma unroll
-        for (int v = 0; v < kRun / 4; ++v) {
+        for (int p = 0; p < kPasses; ++p) {
+            const bool in = y0 + p * kPassIds < V;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = prob(zt[v][i], dr.mt, dr.inv_t, dr.it_s);
-                w[4 * v + i] = dr.zd ? fmaxf(0.f, p - prob(zd[v][i], dr.md, dr.inv_t, dr.id_s)) : p;
+                const float pt = prob(zt[p][i], dr.mt, dr.inv_t, dr.it_s);
+                const float wi = dr.zd ? fmaxf(0.f, pt - prob(zd4[p][i], dr.md, dr.inv_t, dr.id_s)) : pt;
+                w[p][i] = in ? wi : 0.f;
             }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < kRun; ++i) w[i] = (y0 + i < V) ? weight(dr, y0 + i) : 0.f;
-    }
-    float s = 0.f;
+        for (int p = 0; p < kPasses; ++p)
 #pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-        s += w[i];
-        run[i] = s;
+            for (int i = 0; i < 4; ++i) {
+                const int y = y0 + p * kPassIds + i;
+                w[p][i] = y < V ? weight(dr, y) : 0.f;
+            }
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s += w[p][i];
+            run[p][i] = s;
+        }
     }
 }
 
-// Exclusive prefix of v over the workgroup's threads (thread order) and the
-// total, defined as the last thread's exclusive prefix plus its own value.
-__device__ __forceinline__ float block_excl_scan(float v, float* sh, float& total) {
+// Per pass: the exclusive prefix ex[p] of the run totals over the
+// workgroup's threads (inclusive scan in lane order within a wave, then the
+// totals of the earlier waves added in wave order) and the pass total tot[p],
+// defined as the last thread's exclusive prefix plus its own run total.
+// `sh` holds kScanShared floats: the wave totals of pass p at 4p..4p+3, the
+// pass totals after them.
+__device__ __forceinline__ void pass_scan(const float run[kPasses][4], float* sh,
+                                          float ex[kPasses], float tot[kPasses]) {
+    static_assert(kDrawThreads / kWave == 4, "four wave totals per pass");
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    float incl = v;
+    float incl[kPasses];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const float t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
+    for (int p = 0; p < kPasses; ++p) incl[p] = run[p][3];
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1)
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const float t = __shfl_up(incl[p], o, kWave);
+            if (lane >= o) incl[p] += t;
+        }
+    float excl[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        excl[p] = __shfl_up(incl[p], 1, kWave);
+        if (lane == 0) excl[p] = 0.f;
+        if (lane == kWave - 1) sh[4 * p + wave] = incl[p];
     }
-    float excl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) excl = 0.f;
-    if (lane == kWave - 1) sh[wave] = incl;
     __syncthreads();
-    float base = 0.f;
-    for (int w = 0; w < wave; ++w) base += sh[w];
-    const float ex = base + excl;
-    if (tid == kDrawThreads - 1) sh[kDrawThreads / kWave] = ex + v;
+    f32x4 wt[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) wt[p] = *reinterpret_cast<const f32x4*>(sh + 4 * p);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        float base = 0.f;
+        if (wave > 0) base += wt[p][0];
+        if (wave > 1) base += wt[p][1];
+        if (wave > 2) base += wt[p][2];
+        ex[p] = base + excl[p];
+        if (tid == kDrawThreads - 1) sh[4 * kPasses + p] = ex[p] + run[p][3];
+    }
     __syncthreads();
-    total = sh[kDrawThreads / kWave];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) tot[p] = sh[4 * kPasses + p];
     __syncthreads();
-    return ex;
 }
 
-// Chunk total of the draw weights (the same arithmetic as the draw's rescan).
+// Chunk total of the draw weights: the pass totals added in pass order from
+// zero (the same arithmetic as the draw's rescan, whose last prefix it is).
 __device__ __forceinline__ float chunk_total(const DrawRows& dr, int c, int V, float* sh) {
-    float run[kRun];
-    run_sums(dr, c, V, run);
-    float total;
-    block_excl_scan(run[kRun - 1], sh, total);
+    float run[kPasses][4], ex[kPasses], tot[kPasses];
+    pass_runs(dr, c, V, run);
+    pass_scan(run, sh, ex, tot);
+    float total = 0.f;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) total += tot[p];
     return total;
 }
 
@@ -373,7 +426,7 @@ __global__ __launch_bounds__(kDrawThreads) void decide_chunk_kernel(
     const int b = blockIdx.x / nchunk;
     const int c = blockIdx.x - b * nchunk;
     __shared__ int sh_first, sh_bad;
-    __shared__ float sh[kDrawThreads / kWave + 1];
+    __shared__ __align__(16) float sh[kScanShared];
     __shared__ float sh_stat[4];
     const size_t n_t = (size_t)B * (K + 1);
     const int js = decide(target, draft, tokens, b, K, V, nchunk, inv_t, greedy, k0, k1, step, n_t,
@@ -477,7 +530,7 @@ __global__ __launch_bounds__(kDrawThreads) void chunk_total_kernel(
     const float* mb = meta + (size_t)b * kMeta;
     const int js = __float_as_int(mb[0]);
     if (js <= 0) return;                       // no draw for this request
-    __shared__ float sh[kDrawThreads / kWave + 1];
+    __shared__ __align__(16) float sh[kScanShared];
     const bool resid = js <= K;
     DrawRows dr;
     dr.zt = target + ((size_t)b * (K + 1) + js - 1) * V;
@@ -491,21 +544,30 @@ __global__ __launch_bounds__(kDrawThreads) void chunk_total_kernel(
     if (threadIdx.x == 0) ctot[(size_t)b * nchunk + c] = tot;
 }
 
-// Smallest y of chunk c with prefix + C_y > t (C as in run_sums / the block
-// scan); -1 if none.
+// Smallest y of chunk c with prefix + C_y > t, -1 if none.  C_y, the
+// cumulative weight of the chunk's ids up to y, is P_p + (ex[p] + run[p][i])
+// for id y in pass p: P_p is the sum of the earlier passes' totals in pass
+// order, ex and run as in pass_scan / pass_runs.  At the chunk's last id it
+// is the chunk total.
 __device__ int find_in_chunk(const DrawRows& dr, int c, int V, float prefix, float t, float* sh,
                              int* sh_hit) {
-    float run[kRun];
-    run_sums(dr, c, V, run);
-    float total;
-    const float ex = block_excl_scan(run[kRun - 1], sh, total);
+    float run[kPasses][4], ex[kPasses], tot[kPasses];
+    pass_runs(dr, c, V, run);
+    pass_scan(run, sh, ex, tot);
     if (threadIdx.x == 0) *sh_hit = INT_MAX;
     __syncthreads();
-    const int y0 = c * kChunk + kRun * threadIdx.x;
+    const int y0 = c * kChunk + 4 * (int)threadIdx.x;
     int hit = INT_MAX;
+    float P = 0.f;
 #pragma unroll
-    for (int i = kRun - 1; i >= 0; --i)
-        if (y0 + i < V && prefix + (ex + run[i]) > t) hit = y0 + i;
+    for (int p = 0; p < kPasses; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int y = y0 + p * kPassIds + i;
+            if (y < V && prefix + (P + (ex[p] + run[p][i])) > t) hit = min(hit, y);
+        }
+        P += tot[p];
+    }
     if (hit != INT_MAX) atomicMin(sh_hit, hit);
     __syncthreads();
     const int r = *sh_hit;
@@ -526,7 +588,7 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(
     const float* mb = meta + (size_t)b * kMeta;
     const int js = __float_as_int(mb[0]);
     if (js <= 0) return;                       // written by decide_chunk_kernel
-    __shared__ float sh[kDrawThreads / kWave + 1];
+    __shared__ __align__(16) float sh[kScanShared];
     __shared__ float sh_c[2];
     __shared__ int sh_i[2];
     const bool resid = js <= K;

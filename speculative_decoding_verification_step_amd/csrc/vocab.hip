@@ -53,6 +53,8 @@ constexpr int kMeta = 8;                           // per-request words passed t
 // stage at B = 256, V = 128256 (4096 chunk workgroups) 199-201 -> 192-193 us;
 // at 128 (B = 8) and 4 (B = 1) workgroups the extra launch costs 1.4-1.7 us
 constexpr long long kSplitMinGroups = 1024;
+// statistics reads above the last-level cache's size take non-temporal loads
+constexpr double kStreamStatsBytes = 256.0 * 1024 * 1024;
 
 // exp(x) on the transcendental unit: v_exp_f32(x * log2(e)).  Relative error
 // about 2^-24 * |x * log2(e)| + 1 ulp, far inside the 1e-5 decision band for
@@ -88,6 +90,9 @@ __device__ __forceinline__ void arg_merge(float& v, int& i, float v2, int i2) {
 
 // `copy` (optional): the target rows are also written to copy + row *
 // copy_stride (a row of a larger array), from the registers they were read into.
+// kStream: non-temporal loads, for rows too large to stay in the last-level
+// cache (the draw's later re-read of a few rows then misses it anyway).
+template <bool kStream>
 __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, int n_t, int V,
     int nchunk, float inv_t, int greedy, int vec4, float* __restrict__ pv,
@@ -106,7 +111,10 @@ __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(
             const int e = base + 4 * (tid + v * kStatsThreads);
             idx0[v] = e;
             f32x4 q = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            if (e < V) q = *reinterpret_cast<const f32x4*>(z + e);   // V % 4 == 0 here
+            if (e < V) {                                             // V % 4 == 0 here
+                const f32x4* a = reinterpret_cast<const f32x4*>(z + e);
+                q = kStream ? __builtin_nontemporal_load(a) : *a;
+            }
             x[4 * v] = q.x;
             x[4 * v + 1] = q.y;
             x[4 * v + 2] = q.z;
@@ -685,8 +693,15 @@ hipError_t launch_row_stats(const float* target, const float* draft, int n_t, in
                      (draft == nullptr || (uintptr_t)draft % 16 == 0);
     const double copied = copy ? (double)n_t * V * 4.0 : 0.0;
     ProfScope prof("row_stats", stream, (double)rows * V * 4.0 + copied, 0.0);
-    SV_LAUNCH(prof, row_stats_kernel, rows * nchunk, kStatsThreads, stream, target, draft, n_t, V,
-              nchunk, inv_t, greedy, vec4, pv, ps, pi, copy, copy_stride);
+    // beyond the 256 MiB last-level cache the rows stream past it: large batch
+    // (657 MB) 117 -> 100 us; below it the draw's re-read of its rows hits the
+    // cache (70B share, 37 MB: non-temporal loads cost the stage 1.5 us)
+    if ((double)rows * V * 4.0 > kStreamStatsBytes)
+        SV_LAUNCH(prof, row_stats_kernel<true>, rows * nchunk, kStatsThreads, stream, target,
+                  draft, n_t, V, nchunk, inv_t, greedy, vec4, pv, ps, pi, copy, copy_stride);
+    else
+        SV_LAUNCH(prof, row_stats_kernel<false>, rows * nchunk, kStatsThreads, stream, target,
+                  draft, n_t, V, nchunk, inv_t, greedy, vec4, pv, ps, pi, copy, copy_stride);
     return hipGetLastError();
 }
 

@@ -243,8 +243,14 @@ __device__ __forceinline__ float weight(const DrawRows& dr, int y) {
 // thread t owns the run of 4 ids c * kChunk + p * kPassIds + 4t .. +3 (zero
 // past V), so the lanes of a load are 16 B apart and every line a wave
 // touches is read once.  run[p][i] holds the running sum over the run.
+// kStream: non-temporal loads (rows that no later kernel re-reads soon).
+template <bool kStream = false>
 __device__ __forceinline__ void pass_runs(const DrawRows& dr, int c, int V,
                                           float run[kPasses][4]) {
+    auto ld = [](const float* a) {
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(a);
+        return kStream ? __builtin_nontemporal_load(p4) : *p4;
+    };
     const int y0 = c * kChunk + 4 * (int)threadIdx.x;
     float w[kPasses][4];
     const bool vec = (V % 4 == 0) && ((uintptr_t)dr.zt % 16 == 0) &&
@@ -258,13 +264,13 @@ __device__ __forceinline__ void pass_runs(const DrawRows& dr, int c, int V,
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
                 const int y = min(y0 + p * kPassIds, V - 4);
-                zt[p] = *reinterpret_cast<const f32x4*>(dr.zt + y);
-                zd4[p] = *reinterpret_cast<const f32x4*>(dr.zd + y);
+                zt[p] = ld(dr.zt + y);
+                zd4[p] = ld(dr.zd + y);
             }
         } else {
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
-                zt[p] = *reinterpret_cast<const f32x4*>(dr.zt + min(y0 + p * kPassIds, V - 4));
+                zt[p] = ld(dr.zt + min(y0 + p * kPassIds, V - 4));
                 zd4[p] = zt[p];
             }
         }
@@ -346,9 +352,10 @@ __device__ __forceinline__ void pass_scan(const float run[kPasses][4], float* sh
 
 // Chunk total of the draw weights: the pass totals added in pass order from
 // zero (the same arithmetic as the draw's rescan, whose last prefix it is).
+template <bool kStream = false>
 __device__ __forceinline__ float chunk_total(const DrawRows& dr, int c, int V, float* sh) {
     float run[kPasses][4], ex[kPasses], tot[kPasses];
-    pass_runs(dr, c, V, run);
+    pass_runs<kStream>(dr, c, V, run);
     pass_scan(run, sh, ex, tot);
     float total = 0.f;
 #pragma unroll
@@ -548,7 +555,9 @@ __global__ __launch_bounds__(kDrawThreads) void chunk_total_kernel(
     dr.md = mb[3];
     dr.id_s = mb[4];
     dr.inv_t = inv_t;
-    const float tot = chunk_total(dr, c, V, sh);
+    // the split form runs at large batches, whose rows the draw mostly does not
+    // re-read: chunk totals 37.3 -> 34.5 us on the 768-row workload
+    const float tot = chunk_total<true>(dr, c, V, sh);
     if (threadIdx.x == 0) ctot[(size_t)b * nchunk + c] = tot;
 }
 

@@ -21,6 +21,8 @@ namespace sv {
 
 namespace {
 
+constexpr int kNormGroupMaxRows = 256;
+
 template <bool kBf16, bool kMoe, int VPT, int THREADS>
 __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
     const float* src, float* hout,  // src may equal hout
@@ -64,20 +66,39 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
         if constexpr (kHoldGain) g[v] = c < n4 ? g4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (splits > 0) {
-        // acc = part[0] + part[1] + ... per element, planes outermost
+        // acc = part[0] + part[1] + ... per element, planes outermost.  With
+        // few rows (fewer workgroups than CUs) a row's time is its chain of
+        // memory round trips, so the planes are loaded PG at a time (at most 8
+        // vectors per thread in flight): 70B share, 40 rows, 5.7 -> 5.1 us.
+        // With many rows they are loaded one plane at a time across the grid,
+        // which the memory system serves better (768 rows: 14.7 against
+        // 15.4 us grouped).  The additions keep the plane order either way.
+        constexpr int PG = VPT >= 8 ? 1 : 8 / VPT;
+        const int pg = M <= kNormGroupMaxRows ? PG : 1;
         f32x4 acc[VPT];
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const int c = tid + v * THREADS;
-            acc[v] = c < n4 ? reinterpret_cast<const f32x4*>(part + off)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int v = 0; v < VPT; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-        for (int s = 1; s < splits; ++s) {
-            const f32x4* p4 = reinterpret_cast<const f32x4*>(part + s * split_stride + off);
+        for (int s0 = 0; s0 < splits; s0 += pg) {
+            f32x4 pv[PG][VPT];
 #pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                const int c = tid + v * THREADS;
-                if (c < n4) acc[v] += p4[c];
+            for (int j = 0; j < PG; ++j) {
+                const bool in = j < pg && s0 + j < splits;
+                const f32x4* p4 = reinterpret_cast<const f32x4*>(part + (size_t)(s0 + j) * split_stride + off);
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    const int c = tid + v * THREADS;
+                    pv[j][v] = (in && c < n4) ? p4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PG; ++j) {
+                if (j >= pg || s0 + j >= splits) break;
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    if (s0 + j == 0) acc[v] = pv[j][v];
+                    else acc[v] += pv[j][v];
+                }
             }
         }
 #pragma unroll

@@ -73,6 +73,8 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
         // With many rows they are loaded one plane at a time across the grid,
         // which the memory system serves better (768 rows: 14.7 against
         // 15.4 us grouped).  The additions keep the plane order either way.
+        // The planes are dead once read, so they take non-temporal loads (768
+        // rows: the step 2.292 -> 2.285 ms, the down projections 1 us faster).
         constexpr int PG = VPT >= 8 ? 1 : 8 / VPT;
         const int pg = M <= kNormGroupMaxRows ? PG : 1;
         f32x4 acc[VPT];
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
 #pragma unroll
                 for (int v = 0; v < VPT; ++v) {
                     const int c = tid + v * THREADS;
-                    pv[j][v] = (in && c < n4) ? p4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+                    pv[j][v] = (in && c < n4) ? __builtin_nontemporal_load(p4 + c)
+                                              : f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
 #pragma unroll

@@ -96,11 +96,12 @@ __global__ __launch_bounds__(THREADS) void rmsnorm_kernel(
             }
 #pragma unroll
             for (int j = 0; j < PG; ++j) {
-                if (j >= pg || s0 + j >= splits) break;
+                if (j < pg && s0 + j < splits) {
 #pragma unroll
-                for (int v = 0; v < VPT; ++v) {
-                    if (s0 + j == 0) acc[v] = pv[j][v];
-                    else acc[v] += pv[j][v];
+                    for (int v = 0; v < VPT; ++v) {
+                        if (s0 + j == 0) acc[v] = pv[j][v];
+                        else acc[v] += pv[j][v];
+                    }
                 }
             }
         }

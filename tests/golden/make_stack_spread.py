@@ -11,9 +11,12 @@ reference is the spread that rounding alone produces through the stack.  The
 maximum over a few rows is set by the single worst cascade of bf16 rounding
 flips, so it varies between orders; the envelope over the orders (largest
 max and p99.9, mean of the means) is what the GPU is held to.  Calls only
-``workload`` and ``oracle``.
+``workload`` and ``oracle``.  The 8B-shaped sweep (B x K over the same
+stack) takes the first 576 rows, the largest B*(K+1) of the sweep; every
+point of the sweep steps over a prefix of them.
 
-    python tests/golden/make_stack_spread.py
+    python tests/golden/make_stack_spread.py [name ...]   (default: all; the
+    named workloads are recomputed and merged into the existing file)
 """
 import json
 import os
@@ -29,16 +32,22 @@ import workload  # noqa: E402
 from oracle import forward as of  # noqa: E402
 
 ORDERS = (0, 1, 2, 3)
-NAMES = ("8b-shaped-b1-k4", "70b-layer-share-b8-k4", "large-batch-b256-k2")
+# workload -> rows of the step (None: its own B * (K + 1))
+NAMES = {"8b-shaped-b1-k4": None, "70b-layer-share-b8-k4": None, "large-batch-b256-k2": None,
+         "8b-shaped-sweep": max(workload.SWEEP_B) * (max(workload.SWEEP_K) + 1)}
+PATH = os.path.join(HERE, "bf16_stack_spread.json")
 
 
-def main():
+def main(names):
     out = {"note": __doc__.strip().splitlines()[2:14], "workloads": {}}
-    for name in NAMES:
+    if os.path.exists(PATH) and set(names) != set(NAMES):
+        with open(PATH) as f:
+            out["workloads"] = json.load(f)["workloads"]
+    for name in names:
         t0 = time.time()
         w = workload.WORKLOADS[name]
         model = workload.make_model(w, draft_head=False)
-        hidden = workload.make_hidden(w)
+        hidden = workload.make_hidden(w, NAMES[name])
         z64 = of.forward(model, hidden)
         per = []
         for order in ORDERS:
@@ -54,9 +63,9 @@ def main():
                                   "orders": per}
         print(name, out["workloads"][name], f"{time.time() - t0:.0f}s", flush=True)
         del model
-    with open(os.path.join(HERE, "bf16_stack_spread.json"), "w") as f:
+    with open(PATH, "w") as f:
         json.dump(out, f, indent=1)
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1:] or list(NAMES))

@@ -111,6 +111,61 @@ def test_large_batch_step():
 
 
 @gpu
+def test_8b_shaped_sweep_step():
+    """The 8B-shaped sweep: one stack, B in {1, 4, 16, 64} x K in {1, 2, 4, 8}
+    (M = 2 .. 576, so both matmul families and both forms of the decision
+    stage run) at draft noise 0.1 and 0.5, T = 1.  Every point steps over a
+    prefix of the same 576 hidden rows, so one oracle forward (target head
+    and both draft heads) serves them all.  Per point: the step's logits
+    against the oracle's (p99.9 and the envelope of the sweep's 576 rows),
+    and the oracle's rejection sampling on the step's own logits, bit for bit
+    outside the 1e-5 band; at least 35% of all requests compared."""
+    sv = require_gpu()
+    w = workload.WORKLOADS["8b-shaped-sweep"]
+    base = workload.WORKLOADS["8b-shaped-b1-k4"]
+    # the same stack as the B = 1, K = 4 workload: its cached weights serve
+    assert (w.d, w.ffn, w.n_layers, w.vocab, w.wdtype, w.init, w.seed) == \
+        (base.d, base.ffn, base.n_layers, base.vocab, base.wdtype, base.init, base.seed)
+    model = dict(host_workload("8b-shaped-b1-k4")[0])
+    heads = {s: f"w_draft_{s}" for s in workload.SWEEP_SIGMA}
+    for s, key in heads.items():
+        model[key] = workload.make_draft_head(w, model["w_head"], s)
+    Mmax = max(workload.SWEEP_B) * (max(workload.SWEEP_K) + 1)
+    hidden = workload.make_hidden(w, Mmax)
+    note(f"8b-shaped-sweep: oracle forward on {Mmax} rows (target and {len(heads)} draft heads)")
+    zs = of.forward(model, hidden, heads=("w_head", *heads.values()))
+    zt, zd = zs[0], dict(zip(heads, zs[1:]))
+    m = device_model(sv, model, tiled=True)
+    hid_t = torch.from_numpy(hidden).cuda()
+    T, V = w.temperature, w.vocab
+    compared = total = 0
+    for B in workload.SWEEP_B:
+        for K in workload.SWEEP_K:
+            M = B * (K + 1)
+            for i, sigma in enumerate(workload.SWEEP_SIGMA):
+                dl = np.ascontiguousarray(zd[sigma][:M].reshape(B, K + 1, V)[:, :K]).astype(np.float32)
+                x = ov.sample_draft_tokens(dl, T, 0, 0)
+                note(f"8b-shaped-sweep: GPU step B={B} K={K} M={M} sigma={sigma}")
+                logits, out, al = m.step(hid_t[:M].contiguous(), torch.from_numpy(dl).cuda(),
+                                         torch.from_numpy(x).cuda(), B, K, T, 0, 0)
+                torch.cuda.synchronize()
+                z_gpu, out, al = cpu(logits), cpu(out), cpu(al)
+                assert np.all((al >= 1) & (al <= K + 1)), al
+                if i == 0:      # the logits do not depend on the draft
+                    check_full_stack(np.abs(z_gpu.astype(np.float64) - zt[:M]), "8b-shaped-sweep",
+                                     f"sweep B={B} K={K} logits, all {M} rows")
+                ref_out, ref_al, res = ov.verify(z_gpu.astype(np.float64).reshape(B, K + 1, V),
+                                                 dl.astype(np.float64), x, T, 0, 0)
+                near = compare_accept(out, al, ref_out, ref_al, res)
+                compared += B - near
+                total += B
+                note(f"  B={B} K={K} sigma={sigma}: {B - near}/{B} bit-exact on the step's "
+                     f"logits, mean AL {al.mean():.3f}")
+    note(f"8b-shaped-sweep: {compared}/{total} compared bit for bit ({compared / total:.0%})")
+    assert compared >= MIN_COMPARED_SAMPLING * total
+
+
+@gpu
 def test_step_graph_replay_matches_eager():
     """A captured step replays to the eager result, with eager work and
     synchronisation between replays."""

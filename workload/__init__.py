@@ -159,14 +159,19 @@ def make_model(w: Workload, sigma: float | None = None, draft_head: bool = True)
     head32 = _normal((V, d), std, w.seed, _STREAM["w_head"])
     model["w_head"] = _as_weight(head32, w.wdtype)
     if draft_head:
-        # The draft head is built from the *stored* target head (after bf16
-        # rounding) plus the perturbation, then rounded to the weight dtype.
-        base = head32 if w.wdtype == "f32" else bf16_bits_to_f32(model["w_head"])
-        e = _normal((V, d), std, w.seed, _STREAM["e_head"])
-        e *= np.float32(sigma)
-        e += base
-        model["w_draft_head"] = _as_weight(e, w.wdtype)
+        model["w_draft_head"] = make_draft_head(w, model["w_head"], sigma)
     return model
+
+
+def make_draft_head(w: Workload, w_head: np.ndarray, sigma: float) -> np.ndarray:
+    """Draft head W_head + sigma * E for the stored target head `w_head` (bf16
+    bit patterns or fp32, after rounding), rounded to the weight dtype; E is
+    drawn like W_head from its own stream, the same for every sigma."""
+    base = w_head if w.wdtype == "f32" else bf16_bits_to_f32(w_head)
+    e = _normal((w.vocab, w.d), w.weight_std, w.seed, _STREAM["e_head"])
+    e *= np.float32(sigma)
+    e += base
+    return _as_weight(e, w.wdtype)
 
 
 def make_hidden(w: Workload, M: int | None = None, sub: int = 0) -> np.ndarray:

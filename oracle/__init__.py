@@ -20,6 +20,14 @@ the pages it cites:
                   normalize(max(0, p - q)), bonus token after full acceptance;
                   greedy mode at temperature 0.
 * ``laws``     -- closed forms and exact laws used to pin the above.
+* ``attention`` -- causal attention of the verified positions over a paged
+                  KV cache, the append, the commit of the accepted positions
+                  and a block free list.
+* ``moe``      -- the verification forward of a mixture-of-experts target
+                  (top-k routing, SiLU experts, rank-order combine).
+* ``cycle``    -- the draft loop and the whole draft-then-verify cycle.
+* ``dsd``      -- the draft-length choice (goodput-optimal K per batch size)
+                  and the running-average window rule.
 
 Pins (what each function is checked against, outside itself) are listed in
 each module's docstring; none is "parity unpinned".

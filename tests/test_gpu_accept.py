@@ -27,6 +27,11 @@ CASES = [
     (4, 3, 3000, 3.0, 1.0, 2.0),           # high temperature: acceptance collapse
     (3, 20, 5000, 1.0, 1.5, 0.2),          # long drafts: five positions per wave
     (1024, 1, 4096, 1.0, 1.5, 0.4),        # many short requests: 1024 chunk groups, split form
+    (4, 4, 3000, 0.05, 1.5, 0.3),          # sharp: most probabilities underflow to zero
+    (3, 3, 1, 1.0, 1.0, 0.5),              # one-token vocabulary: p = q = 1
+    (3, 3, 1, 0.0, 1.0, 0.5),
+    (5, 2, 2, 1.0, 1.0, 1.0),              # two tokens
+    (5, 2, 3, 0.0, 1.0, 1.0),
 ]
 
 

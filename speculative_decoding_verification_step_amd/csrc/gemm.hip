@@ -36,7 +36,9 @@
 // deterministic).  Tile order: workgroup i runs on XCD i % 8, so tiles are
 // renumbered to give every XCD a contiguous run, activation tile fastest:
 // the tiles that share one weight panel run together on one XCD and reuse it
-// from that XCD's L2.
+// from that XCD's L2.  The K split is the slowest index, so an XCD's run
+// stays within one split and reads only that split's share of the
+// activations (768-row down projection, 4 splits: 79.4 -> 78.3 us).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -101,15 +103,16 @@ void mfma_gemm_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restric
     const int wn = wave / WM, wm = wave % WM;
 
     // XCD-contiguous renumbering (XCD x = i % 8 gets G/8 tiles, the first
-    // G%8 XCDs one more), then activation tile fastest, K split next, weight
-    // tile slowest
+    // G%8 XCDs one more), then activation tile fastest, weight tile next, K
+    // split slowest
     const int G = gridDim.x, L = blockIdx.x;
     const int q = G / 8, r = G % 8, x = L % 8, j8 = L / 8;
     const int t = x < r ? x * (q + 1) + j8 : r * (q + 1) + (x - r) * q + j8;
     const int MT = (M + BM32 * 32 - 1) / (BM32 * 32);
+    const int NT = (N + BN32 * 32 - 1) / (BN32 * 32);
     const int tm = t % MT;
-    const int split = (t / MT) % splits;
-    const int tn = t / (MT * splits);
+    const int tn = (t / MT) % NT;
+    const int split = t / (MT * NT);
     const int S = K / 32;
     const int s_begin = split * steps_per_split;
     const int nsteps = min(S, s_begin + steps_per_split) - s_begin;   // >= 1 (launcher)

@@ -891,7 +891,8 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
-              "(the step is data-parallel over requests; see the design notes for sharding)",
+              "(requests are independent: several GPUs would each verify their own share of "
+              "the batch, and this program measures one)",
               file=sys.stderr)
         sys.exit(2)
     import torch

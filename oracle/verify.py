@@ -20,8 +20,7 @@ The rule, as the pages state it:
   the output of plain greedy decoding (same section; klu.ai "Mathematical
   Guarantee").
 
-Readings where the pages are silent (each is stated again in the design
-notes):
+Readings where the pages are silent:
 
 * K + 1 target rows per request: row j (0-based) holds p for draft token j,
   row K the bonus distribution.

@@ -206,6 +206,26 @@ def test_large_batch_weights_ragged_rows(M):
 
 
 @gpu
+@pytest.mark.parametrize("M", [1000, 2049])
+def test_lds_gemm_beyond_768_rows(M):
+    """Row counts beyond the large batch's 768, in the tiles the library picks
+    there: several activation tiles per weight panel, more than one round of
+    256 workgroups and a K-split down projection, ragged at 2049.  Sampled
+    rows at tile edges and the tail against the oracle (rows are
+    independent)."""
+    sv = require_gpu()
+    w = workload.Workload("tiles-bf16", 512, 4096, 2, 9001, "bf16", 1, 4, 0.3, 1.0, "std_0.02", 7)
+    model = workload.make_model(w, draft_head=False)
+    m = device_model(sv, model, tiled=True)
+    h = workload.make_hidden(w, M, sub=M)
+    z = cpu(m.forward(torch.from_numpy(h).cuda()))
+    assert np.all(np.isfinite(z))
+    rows = sorted({0, 1, 63, 64, 191, 192, 255, 256, 383, 384, 511, 512, 767, 768, 1023 % M,
+                   M // 2, M - 2, M - 1})
+    _check(z[rows], of.forward(model, h[rows]), TOL_BF16, f"LDS GEMM M={M} rows {rows}")
+
+
+@gpu
 @pytest.mark.parametrize("tile", ["256", "192", "128", "64"])
 @pytest.mark.parametrize("M", [129, 200, 333])
 def test_lds_gemm_every_tile(tile, M, monkeypatch):
